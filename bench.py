@@ -1,0 +1,350 @@
+"""Benchmark: bf16 -> fp32 GEMM TFLOP/s and fraction of the MFMA roof at 4096^3, plus the
+skinny decode shapes' HBM GB/s, on one MI355X. Prints ONE JSON line.
+
+A step is one call of the library's dispatching entry point (gemm_bf16) on the 4096^3 workload
+(A, B ~ N(0,1) bf16 from fixed seeds, already resident in HBM). `value` is the throughput of
+the K timed steps, run back to back on one stream between two synchronisations. The dominant
+kernel's average duration is also measured with HIP events recorded on the stream the kernel
+is launched on, and gives `roofline.achieved` = 2*M*N*K / duration.
+
+Alongside (reported, not part of `value`):
+* the card's measured roofs: sustained MFMA bf16->fp32 TFLOP/s and shader clock, HBM copy and
+  read GB/s over 1 GiB buffers, and the empty-launch floor;
+* every decode workload (M = 1, 2, 16, 64 against the 7B MLP weights), timed over 12 rotating
+  copies of the weights (> 1 GiB, more than the 256 MB Infinity Cache) so each call reads cold
+  weights, as single launches between events and back to back;
+* the float64 CPU oracle timed on a bounded row sample of the same 4096^3 product
+  (cpu_baseline), and torch.matmul (hipBLASLt) at 4096^3 as a comparison only.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "bf16→fp32 GEMM TFLOP/s & % MFMA peak at 4096³; skinny M≤64 HBM GB/s"
+MI355X_PEAK_BF16_TFLOPS = 2500.0   # published dense bf16 MFMA peak
+MI355X_PEAK_HBM_GBPS = 8000.0      # published HBM3E bandwidth
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sq4096")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the roof microbenchmarks")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--large", action="store_true", help="also time sq8192, sq16384, mlp_up/down")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemv_layers_amd as g
+    from synth import WORKLOADS, matrix
+
+    torch.cuda.set_device(0)
+    g.gemm_init(0)
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def dev(h):
+        return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).view(torch.bfloat16).cuda()
+
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    out = {}
+
+    # ---------------- measured roofs ----------------
+    peaks = {}
+    if not args.no_peaks:
+        log("MFMA peak")
+        blocks = 512
+        sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda")
+        cyc = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+        flop_per_iter = blocks * 4 * 8 * 32768
+
+        def mfma_run(iters):
+            e0, e1 = events(2)
+            e0.record(stream)
+            g.gemm_peak_mfma_launch(iters, blocks, P(sink), P(cyc), sh)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            c = cyc.view(-1, 2).double()
+            clk_ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1  # s_memrealtime runs at 100 MHz
+            return flop_per_iter * iters / (ms * 1e-3) / 1e12, ms, clk_ghz
+
+        mfma_run(20000)  # clock ramp
+        t_end = time.time() + 0.3
+        while time.time() < t_end:
+            mfma_run(20000)
+        burst = max(mfma_run(20000)[0] for _ in range(3))
+        sus_tf, sus_ms, sus_clk = mfma_run(5_000_000)
+        peaks["mfma_bf16_fp32_tflops_burst"] = round(burst, 1)
+        peaks["mfma_bf16_fp32_tflops_sustained"] = round(sus_tf, 1)
+        peaks["mfma_sustained_ms"] = round(sus_ms, 1)
+        peaks["shader_clock_ghz_sustained"] = round(sus_clk, 3)
+
+        log("HBM copy/read")
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        g.gemm_fill_launch(P(src), nbytes, 0x12345678, sh)
+        rsink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+        best_copy = best_read = 0.0
+        for _ in range(10):
+            e0, e1, e2 = events(3)
+            e0.record(stream)
+            g.gemm_peak_copy_launch(P(src), P(dst), nbytes, sh)
+            e1.record(stream)
+            g.gemm_peak_read_launch(P(src), nbytes, P(rsink), sh)
+            e2.record(stream)
+            torch.cuda.synchronize()
+            best_copy = max(best_copy, 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+            best_read = max(best_read, nbytes / (e1.elapsed_time(e2) * 1e-3) / 1e9)
+        e0, e1 = events(2)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        peaks["hbm_copy_gbps"] = round(best_copy, 1)
+        peaks["hbm_read_gbps"] = round(best_read, 1)
+        peaks["hip_memcpy_d2d_gbps"] = round(2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        del src, dst
+
+        # launch floor: single launch between events, and back to back
+        singles = []
+        for _ in range(50):
+            e0, e1 = events(2)
+            e0.record(stream)
+            g.gemm_peak_empty_launch(sh)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            singles.append(e0.elapsed_time(e1) * 1e3)
+        e0, e1 = events(2)
+        e0.record(stream)
+        for _ in range(1000):
+            g.gemm_peak_empty_launch(sh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        peaks["empty_launch_us_single_median"] = round(float(np.median(singles)), 2)
+        peaks["empty_launch_us_back_to_back"] = round(e0.elapsed_time(e1), 3)  # ms/1000 = us
+        out["measured_peaks"] = peaks
+
+    # ---------------- the headline workload ----------------
+    w = WORKLOADS[args.workload]
+    log(f"workload {w.name} {w.M}x{w.N}x{w.K}")
+    A = dev(matrix("normal", w.M, w.K, seed=w.seed_a, sigma=w.sigma_a))
+    B = dev(matrix("normal", w.K, w.N, seed=w.seed_b, sigma=w.sigma_b))
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        g.gemm_bf16(w.M, w.N, w.K, P(A), w.K, P(B), w.N, P(C), w.N, sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    plan = g.gemm_last_plan()
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = w.flops / (elapsed / args.steps) / 1e12
+
+    # per-launch kernel duration with events on the launch stream
+    n_ev = max(10, args.steps)
+    evs = events(n_ev + 1)
+    evs[0].record(stream)
+    for i in range(n_ev):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    durs = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n_ev)])  # ms
+    kern_ms = float(durs.mean())
+    achieved = w.flops / (kern_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MI355X_PEAK_BF16_TFLOPS, 4),
+                "traffic": None}
+    headline = {"kernel_us_mean": round(kern_ms * 1e3, 2),
+                "kernel_us_min": round(float(durs.min()) * 1e3, 2),
+                "kernel_us_median": round(float(np.median(durs)) * 1e3, 2),
+                "tflops_best": round(w.flops / (float(durs.min()) * 1e-3) / 1e12, 1),
+                "plan": {k: plan.get(k) for k in ("kernel", "bm", "bn", "grid", "schedule",
+                                                  "splits", "waves", "wave_eff")}}
+    if "mfma_bf16_fp32_tflops_sustained" in peaks:
+        headline["frac_of_measured_mfma_peak"] = round(
+            achieved / peaks["mfma_bf16_fp32_tflops_sustained"], 4)
+
+    # hipBLASLt through torch.matmul, comparison only
+    try:
+        for _ in range(5):
+            torch.matmul(A, B)
+        e0, e1 = events(2)
+        e0.record(stream)
+        for _ in range(20):
+            torch.matmul(A, B)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        headline["torch_matmul_tflops"] = round(w.flops / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12, 1)
+    except Exception as exc:  # comparison arm only
+        headline["torch_matmul_error"] = str(exc)[:200]
+    out["headline"] = headline
+    del A, B, C
+
+    # ---------------- decode workloads (HBM bound) ----------------
+    if not args.no_decode:
+        dec = {}
+        copies = 12
+        shapes = {}
+        for name in sorted(n for n in WORKLOADS if n.startswith("dec_")):
+            wd = WORKLOADS[name]
+            key = (wd.K, wd.N)
+            if key not in shapes:
+                log(f"decode weights {wd.K}x{wd.N} x{copies}")
+                b0 = dev(matrix("normal", wd.K, wd.N, seed=wd.seed_b, sigma=wd.sigma_b))
+                shapes[key] = [b0] + [b0.clone() for _ in range(copies - 1)]
+            Bs = shapes[key]
+            Ad = dev(matrix("normal", wd.M, wd.K, seed=wd.seed_a, sigma=wd.sigma_a))
+            Cd = torch.empty((wd.M, wd.N), dtype=torch.bfloat16, device="cuda")
+
+            def call(b):
+                g.gemm_bf16(wd.M, wd.N, wd.K, P(Ad), wd.K, P(b), wd.N, P(Cd), wd.N, sh)
+
+            for i in range(2 * copies):
+                call(Bs[i % copies])
+            torch.cuda.synchronize()
+            singles = []
+            for i in range(48):
+                e0, e1 = events(2)
+                e0.record(stream)
+                call(Bs[i % copies])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                singles.append(e0.elapsed_time(e1) * 1e3)
+            nb = 96
+            e0, e1 = events(2)
+            e0.record(stream)
+            for i in range(nb):
+                call(Bs[i % copies])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            b2b_us = e0.elapsed_time(e1) * 1e3 / nb
+            single_us = float(np.median(singles))
+            rec = {"us_single_median": round(single_us, 2),
+                   "us_single_min": round(float(np.min(singles)), 2),
+                   "us_back_to_back": round(b2b_us, 2),
+                   "gbps_single": round(wd.bytes / (single_us * 1e-6) / 1e9, 1),
+                   "gbps_back_to_back": round(wd.bytes / (b2b_us * 1e-6) / 1e9, 1),
+                   "plan_splits": g.gemm_last_plan().get("splits")}
+            if "hbm_copy_gbps" in peaks:
+                rec["frac_of_measured_copy"] = round(rec["gbps_back_to_back"] / peaks["hbm_copy_gbps"], 4)
+            dec[name] = rec
+            del Ad, Cd
+        del shapes
+        out["decode"] = dec
+
+    # ---------------- more compute-bound workloads ----------------
+    if args.large:
+        big = {}
+        for name in ("sq8192", "sq16384", "mlp_up", "mlp_down", "sq512"):
+            wl = WORKLOADS[name]
+            log(f"large {name}")
+            Al = dev(matrix("normal", wl.M, wl.K, seed=wl.seed_a, sigma=wl.sigma_a))
+            Bl = dev(matrix("normal", wl.K, wl.N, seed=wl.seed_b, sigma=wl.sigma_b))
+            Cl = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+            n = 20 if wl.flops < 2e12 else 5
+            for _ in range(3):
+                g.gemm_bf16(wl.M, wl.N, wl.K, P(Al), wl.K, P(Bl), wl.N, P(Cl), wl.N, sh)
+            evl = events(n + 1)
+            evl[0].record(stream)
+            for i in range(n):
+                g.gemm_bf16(wl.M, wl.N, wl.K, P(Al), wl.K, P(Bl), wl.N, P(Cl), wl.N, sh)
+                evl[i + 1].record(stream)
+            torch.cuda.synchronize()
+            d = np.array([evl[i].elapsed_time(evl[i + 1]) for i in range(n)])
+            rec = {"us_mean": round(float(d.mean()) * 1e3, 2),
+                   "tflops_mean": round(wl.flops / (float(d.mean()) * 1e-3) / 1e12, 1),
+                   "tflops_best": round(wl.flops / (float(d.min()) * 1e-3) / 1e12, 1)}
+            if "mfma_bf16_fp32_tflops_sustained" in peaks:
+                rec["frac_of_measured_mfma_peak"] = round(
+                    rec["tflops_mean"] / peaks["mfma_bf16_fp32_tflops_sustained"], 4)
+            big[name] = rec
+            del Al, Bl, Cl
+        out["large"] = big
+
+    # ---------------- CPU oracle baseline ----------------
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        log("cpu oracle baseline")
+        Ah = matrix("normal", w.M, w.K, seed=w.seed_a, sigma=w.sigma_a)
+        Bh = matrix("normal", w.K, w.N, seed=w.seed_b, sigma=w.sigma_b)
+        threads = oracle.default_threads()
+        rows_done, t_cpu = 0, 0.0
+        block = 64
+        while t_cpu < args.cpu_seconds and rows_done < w.M:
+            nr = min(block, w.M - rows_done)
+            t1 = time.perf_counter()
+            oracle.gemm_rows(Ah, Bh, rows_done, nr, w.N, w.K, with_abs=True, threads=threads)
+            t_cpu += time.perf_counter() - t1
+            rows_done += nr
+        flops = 2.0 * rows_done * w.N * w.K
+        cpu = {"value": round(flops / t_cpu / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"rows 0..{rows_done - 1} of the {w.name} product "
+                         f"({rows_done}x{w.N}x{w.K}, float64 value and |a*b| sums), {t_cpu:.1f} s"}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "inputs": f"A~N(0,{w.sigma_a}), B~N(0,{w.sigma_b}) bf16, seeds "
+                             f"{w.seed_a:#x}/{w.seed_b:#x}", "parallelism": "none"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    line.update(out)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

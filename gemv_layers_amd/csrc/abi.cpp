@@ -1,0 +1,294 @@
+// The library's C ABI (declared in include/gemm_bf16.h): argument validation on the host before
+// any HIP call, per-device state and workspace, planning and dispatch onto the caller's stream.
+
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/gemm_bf16.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Workspace per device: float32 partial slots for split tiles / K slices, and their counters.
+constexpr int64_t kWsFloats = int64_t(32) << 20;  // 128 MiB
+constexpr int64_t kWsCounters = int64_t(1) << 16;
+
+struct DeviceState {
+    bool ready = false;
+    glk::DeviceInfo info;
+    float* ws = nullptr;
+    uint32_t* counters = nullptr;
+};
+
+std::mutex g_mu;
+DeviceState g_dev[kMaxDevices];
+int g_ready_count = 0;
+std::string g_last_plan = "{}";
+
+int copy_out(const std::string& s, char* buf, int len) {
+    if (!buf || len <= 0) return GEMM_ERR_INVALID_ARG;
+    const size_t n = s.size();
+    if (n + 1 > (size_t)len) {
+        memcpy(buf, s.data(), (size_t)len - 1);
+        buf[len - 1] = '\0';
+        return GEMM_ERR_INVALID_ARG;
+    }
+    memcpy(buf, s.c_str(), n + 1);
+    return GEMM_OK;
+}
+
+int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+             int64_t ldb, const void* C, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+    if (ldc < N || ldc < 0) return GEMM_ERR_INVALID_ARG;
+    if (lda < K || ldb < N) return GEMM_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && C == nullptr) return GEMM_ERR_INVALID_ARG;
+    if (M > 0 && K > 0 && A == nullptr) return GEMM_ERR_INVALID_ARG;
+    if (K > 0 && N > 0 && B == nullptr) return GEMM_ERR_INVALID_ARG;
+    return GEMM_OK;
+}
+
+// force: 0 dispatch on M, 1 skinny, 2 large-tile family
+int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+        void* C, int64_t ldc, hipStream_t stream, int force) {
+    int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != GEMM_OK) return st;
+    if (force == 1 && (M < 1 || M > 64)) return GEMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (g_ready_count == 0) return GEMM_ERR_NOT_INITIALIZED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMM_ERR_HIP;
+    DeviceState& ds = g_dev[dev];
+    if (!ds.ready) return GEMM_ERR_NOT_INITIALIZED;
+
+    const bool fast = glk::fast_path_ok(M, N, K, A, lda, B, ldb, C, ldc);
+    const glk::Plan p = glk::make_plan(M, N, K, ds.info, fast, force);
+    const uint16_t* a16 = static_cast<const uint16_t*>(A);
+    const uint16_t* b16 = static_cast<const uint16_t*>(B);
+    uint16_t* c16 = static_cast<uint16_t*>(C);
+    hipError_t e = hipSuccess;
+    switch (p.kernel) {
+        case glk::kKernNone:
+            break;
+        case glk::kKernZero:
+            e = glk::launch_zero_c(c16, M, N, ldc, stream);
+            break;
+        case glk::kKernGeneric:
+            e = glk::launch_generic_gemm(a16, b16, c16, M, N, K, lda, ldb, ldc, stream);
+            break;
+        case glk::kKernTile: {
+            glk::TileArgs t;
+            t.A = a16;
+            t.B = b16;
+            t.C = c16;
+            t.M = (int)M;
+            t.N = (int)N;
+            t.K = (int)K;
+            t.lda = (int)lda;
+            t.ldb = (int)ldb;
+            t.ldc = (int)ldc;
+            t.tiles_m = (int)p.tiles_m;
+            t.tiles_n = (int)p.tiles_n;
+            t.group_m = p.group_m;
+            t.nxcd = p.nxcd;
+            t.sched = p.sched;
+            t.splits = p.splits;
+            t.kt_per_split = p.kt_per_split;
+            t.ws = ds.ws;
+            t.counters = ds.counters;
+            e = glk::launch_tile_gemm(p.tile_cfg, t, (int)p.grid, stream);
+            break;
+        }
+        case glk::kKernSkinny: {
+            glk::SkinnyArgs s;
+            s.A = a16;
+            s.B = b16;
+            s.C = c16;
+            s.M = (int)M;
+            s.N = (int)N;
+            s.K = (int)K;
+            s.lda = (int)lda;
+            s.ldb = (int)ldb;
+            s.ldc = (int)ldc;
+            s.strips = p.strips;
+            s.splits = p.splits;
+            s.kb_per_split = p.kb_per_split;
+            s.ws = ds.ws;
+            s.counters = ds.counters;
+            e = glk::launch_skinny_gemm(p.mtiles, s, stream);
+            break;
+        }
+        default:
+            return GEMM_ERR_UNSUPPORTED;
+    }
+    if (e != hipSuccess) return GEMM_ERR_HIP;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_last_plan = glk::plan_json(p, M, N, K);
+    }
+    return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_init(int device) {
+    if (device < 0 || device >= kMaxDevices) return GEMM_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_mu);
+    DeviceState& ds = g_dev[device];
+    if (ds.ready) return GEMM_OK;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device >= count) return GEMM_ERR_HIP;
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return GEMM_ERR_HIP;
+    if (hipSetDevice(device) != hipSuccess) return GEMM_ERR_HIP;
+    int rc = GEMM_OK;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) rc = GEMM_ERR_HIP;
+    if (rc == GEMM_OK) {
+        ds.info.cus = prop.multiProcessorCount;
+        ds.info.nxcd = 8;  // MI355X: 8 XCDs, workgroups dealt round robin
+        if (ds.info.cus % ds.info.nxcd != 0) ds.info.nxcd = 1;
+        ds.info.ws_floats = kWsFloats;
+        ds.info.ws_counters = kWsCounters;
+        if (hipMalloc(&ds.ws, kWsFloats * sizeof(float)) != hipSuccess) rc = GEMM_ERR_HIP;
+    }
+    if (rc == GEMM_OK && hipMalloc(&ds.counters, kWsCounters * sizeof(uint32_t)) != hipSuccess)
+        rc = GEMM_ERR_HIP;
+    if (rc == GEMM_OK && hipMemset(ds.counters, 0, kWsCounters * sizeof(uint32_t)) != hipSuccess)
+        rc = GEMM_ERR_HIP;
+    if (rc == GEMM_OK && glk::configure_skinny_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
+    if (rc == GEMM_OK && hipDeviceSynchronize() != hipSuccess) rc = GEMM_ERR_HIP;
+    if (rc == GEMM_OK) {
+        ds.ready = true;
+        ++g_ready_count;
+    } else {
+        if (ds.ws) hipFree(ds.ws);
+        if (ds.counters) hipFree(ds.counters);
+        ds.ws = nullptr;
+        ds.counters = nullptr;
+    }
+    hipSetDevice(prev);
+    return rc;
+}
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+              int64_t ldb, void* C, int64_t ldc, gemm_stream_t stream) {
+    return run(M, N, K, A, lda, B, ldb, C, ldc, reinterpret_cast<hipStream_t>(stream), 0);
+}
+
+int gemm_bf16_skinny(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, void* C, int64_t ldc, gemm_stream_t stream) {
+    return run(M, N, K, A, lda, B, ldb, C, ldc, reinterpret_cast<hipStream_t>(stream), 1);
+}
+
+int gemm_bf16_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                    int64_t ldb, void* C, int64_t ldc, gemm_stream_t stream) {
+    return run(M, N, K, A, lda, B, ldb, C, ldc, reinterpret_cast<hipStream_t>(stream), 2);
+}
+
+int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int skinny, char* buf, int len) {
+    if (M < 0 || N < 0 || K < 0 || cus <= 0) return GEMM_ERR_INVALID_ARG;
+    if (skinny && (M < 1 || M > 64)) return GEMM_ERR_UNSUPPORTED;
+    glk::DeviceInfo dev;
+    dev.cus = cus;
+    dev.nxcd = (cus % 8 == 0) ? 8 : 1;
+    dev.ws_floats = kWsFloats;
+    dev.ws_counters = kWsCounters;
+    const glk::Plan p = glk::make_plan(M, N, K, dev, true, skinny ? 1 : 0);
+    return copy_out(glk::plan_json(p, M, N, K), buf, len);
+}
+
+int gemm_wave_efficiency(int64_t ctas, int64_t slots, double* efficiency, int64_t* waves) {
+    if (ctas < 0 || slots <= 0 || !efficiency || !waves) return GEMM_ERR_INVALID_ARG;
+    glk::wave_efficiency(ctas, slots, efficiency, waves);
+    return GEMM_OK;
+}
+
+int gemm_last_plan(char* buf, int len) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return copy_out(g_last_plan, buf, len);
+}
+
+const char* gemm_status_string(int status) {
+    switch (status) {
+        case GEMM_OK: return "GEMM_OK";
+        case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG";
+        case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED";
+        case GEMM_ERR_NOT_INITIALIZED: return "GEMM_ERR_NOT_INITIALIZED";
+        case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+        default: return "GEMM_ERR_UNKNOWN";
+    }
+}
+
+int gemm_finalize(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    int rc = GEMM_OK;
+    for (int d = 0; d < kMaxDevices; ++d) {
+        DeviceState& ds = g_dev[d];
+        if (!ds.ready) continue;
+        int prev = -1;
+        hipGetDevice(&prev);
+        hipSetDevice(d);
+        if (ds.ws && hipFree(ds.ws) != hipSuccess) rc = GEMM_ERR_HIP;
+        if (ds.counters && hipFree(ds.counters) != hipSuccess) rc = GEMM_ERR_HIP;
+        ds.ws = nullptr;
+        ds.counters = nullptr;
+        ds.ready = false;
+        hipSetDevice(prev);
+    }
+    g_ready_count = 0;
+    return rc;
+}
+
+int gemm_peak_mfma_launch(int64_t iters, int blocks, float* sink, uint64_t* cycles,
+                          gemm_stream_t stream) {
+    if (iters < 0 || blocks <= 0 || !sink || !cycles) return GEMM_ERR_INVALID_ARG;
+    return glk::launch_peak_mfma(iters, blocks, sink, cycles, reinterpret_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
+int gemm_peak_copy_launch(const void* src, void* dst, int64_t bytes, gemm_stream_t stream) {
+    if (bytes < 0 || (bytes & 15) || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15))
+        return GEMM_ERR_INVALID_ARG;
+    if (bytes > 0 && (!src || !dst)) return GEMM_ERR_INVALID_ARG;
+    if (bytes == 0) return GEMM_OK;
+    return glk::launch_peak_copy(src, dst, bytes, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
+int gemm_peak_read_launch(const void* src, int64_t bytes, uint32_t* sink, gemm_stream_t stream) {
+    if (bytes < 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15) || !sink)
+        return GEMM_ERR_INVALID_ARG;
+    if (bytes > 0 && !src) return GEMM_ERR_INVALID_ARG;
+    if (bytes == 0) return GEMM_OK;
+    return glk::launch_peak_read(src, bytes, sink, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
+int gemm_peak_empty_launch(gemm_stream_t stream) {
+    return glk::launch_peak_empty(reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? GEMM_OK
+                                                                                       : GEMM_ERR_HIP;
+}
+
+int gemm_fill_launch(void* dst, int64_t bytes, uint32_t value, gemm_stream_t stream) {
+    if (bytes < 0 || (bytes & 3) || (reinterpret_cast<uintptr_t>(dst) & 15)) return GEMM_ERR_INVALID_ARG;
+    if (bytes > 0 && !dst) return GEMM_ERR_INVALID_ARG;
+    if (bytes == 0) return GEMM_OK;
+    return glk::launch_fill(dst, bytes, value, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Host-visible launch interfaces of the library's kernels (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace glk {
+
+// ---- large-tile MFMA GEMM -------------------------------------------------------------------
+
+// How the flattened work of a launch is cut. Data-parallel: one workgroup per output tile.
+// Split: tile t's K range is cut into `splits` contiguous pieces of `kt_per_split` k-steps, one
+// workgroup per piece; pieces meet in a per-tile float32 fixup summed in K order.
+enum TileSchedule : int { kSchedDataParallel = 0, kSchedSplitK = 1 };
+
+struct TileArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    uint16_t* C;
+    int M, N, K;
+    int lda, ldb, ldc;
+    int tiles_m, tiles_n;
+    int group_m;        // tile rows per group of the grouped (L2-friendly) tile order
+    int nxcd;           // XCDs the hardware deals workgroups over (8 on MI355X), 1 = no remap
+    int sched;          // TileSchedule
+    int splits;         // pieces per tile (split schedule)
+    int kt_per_split;   // k-steps (of 64) per piece (split schedule)
+    float* ws;          // split partial slots, splits * tiles * BM * BN floats
+    uint32_t* counters; // one per tile, zero between launches
+};
+
+// Tile configurations compiled into the library.
+enum TileConfig : int {
+    kTile256x256w4 = 0,  // 256 x 256 tile, 4 waves of 128 x 128
+    kTile256x256w8 = 1,  // 256 x 256 tile, 8 waves of 128 x 64
+    kTile128x128w4 = 2,  // 128 x 128 tile, 4 waves of 64 x 64
+    kTileConfigCount
+};
+
+struct TileShape {
+    int bm, bn, bk, threads;
+};
+TileShape tile_shape(int cfg);
+hipError_t launch_tile_gemm(int cfg, const TileArgs& a, int grid, hipStream_t s);
+
+// ---- general fallback (any alignment / leading dimension) ----------------------------------
+hipError_t launch_generic_gemm(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M,
+                               int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                               hipStream_t s);
+
+// ---- skinny-M weight-streaming GEMM ---------------------------------------------------------
+struct SkinnyArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    uint16_t* C;
+    int M, N, K;
+    int lda, ldb, ldc;
+    int strips;          // column strips of B (width kSkinnyStrip columns)
+    int splits;          // K slices per strip
+    int kb_per_split;    // 32-row k-blocks per slice
+    float* ws;           // splits * strips * 64 * kSkinnyStrip floats
+    uint32_t* counters;  // one per strip, zero between launches
+};
+constexpr int kSkinnyStrip = 128;   // columns per workgroup
+constexpr int kSkinnyKBlock = 32;   // k rows per wave step
+hipError_t launch_skinny_gemm(int mtiles, const SkinnyArgs& a, hipStream_t s);
+hipError_t configure_skinny_kernels();
+
+// ---- misc ------------------------------------------------------------------------------------
+hipError_t launch_zero_c(uint16_t* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
+hipError_t launch_fill(void* dst, int64_t bytes, uint32_t value, hipStream_t s);
+hipError_t launch_peak_mfma(int64_t iters, int blocks, float* sink, uint64_t* cycles,
+                            hipStream_t s);
+hipError_t launch_peak_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+hipError_t launch_peak_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_peak_empty(hipStream_t s);
+
+}  // namespace glk

@@ -1,0 +1,185 @@
+// Host planner. The choices follow the pages' closed forms:
+// * wave efficiency (tiles / slots) / ceil(tiles / slots) decides whether a tile shape fills the
+//   card ("Kernel development on sm_120", section 4, budget 4; spark-kernels "170 is 2 times 5
+//   times 17": a grid that leaves a partial last wave wastes the idle slots for a whole wave);
+// * the tile is picked per call: the big tile when its grid fills at least one wave, otherwise
+//   a smaller tile, otherwise K is split across the idle slots (spark-kernels, "1024 cubed and the
+//   decode shapes" and "170 is 2 times 5 times 17");
+// * M <= 64 streams the weights with the skinny kernel, one workgroup per column strip, K split
+//   just enough to give the card enough workgroups (spark-kernels, "the decode kernel").
+// No autotuning at run time: fixed constants, one closed form per decision ("Kernel development
+// on sm_120", section 6, "Autotune").
+
+#include "plan.h"
+
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace glk {
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+void wave_efficiency(int64_t ctas, int64_t slots, double* eff, int64_t* waves) {
+    if (ctas <= 0 || slots <= 0) {
+        if (eff) *eff = 0.0;
+        if (waves) *waves = 0;
+        return;
+    }
+    const int64_t w = cdiv(ctas, slots);
+    if (waves) *waves = w;
+    if (eff) *eff = ((double)ctas / (double)slots) / (double)w;
+}
+
+bool fast_path_ok(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                  int64_t ldb, const void* C, int64_t ldc) {
+    const int64_t kMaxLd = int64_t(1) << 20, kMaxDim = int64_t(1) << 26;
+    auto aligned16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return false;
+    if ((N & 7) || (K & 7) || (lda & 7) || (ldb & 7) || (ldc & 7)) return false;
+    if (lda > kMaxLd || ldb > kMaxLd || ldc > kMaxLd) return false;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return false;
+    return true;
+}
+
+static void finish_waves(Plan& p) { wave_efficiency(p.grid, p.slots, &p.wave_eff, &p.waves); }
+
+static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+    Plan p;
+    p.kernel = kKernSkinny;
+    p.mtiles = (int)cdiv(M, 16);
+    p.threads = 256;
+    p.strips = (int)cdiv(N, kSkinnyStrip);
+    const int64_t kblocks = cdiv(K, kSkinnyKBlock);
+    const int per_cu = p.mtiles <= 2 ? 2 : 1;  // LDS for the wave sum is 32 KB per 16-row tile
+    const int64_t target = (int64_t)dev.cus * per_cu;
+    int64_t s = std::max<int64_t>(1, (target + p.strips / 2) / p.strips);
+    s = std::min<int64_t>(s, kblocks);
+    const int64_t slot_floats = (int64_t)32 * p.mtiles * 64;
+    while (s > 1 && (int64_t)p.strips * s * slot_floats > dev.ws_floats) --s;
+    if (s > 1 && p.strips > dev.ws_counters) s = 1;
+    p.kb_per_split = (int)cdiv(kblocks, s);
+    p.splits = (int)cdiv(kblocks, p.kb_per_split);
+    p.grid = (int64_t)p.strips * p.splits;
+    p.slots = (int64_t)dev.cus * per_cu;
+    if (p.splits > 1) {
+        p.ws_floats = (int64_t)p.strips * p.splits * slot_floats;
+        p.counters = p.strips;
+    }
+    finish_waves(p);
+    p.reason = "M <= 64: weights streamed once, " + std::to_string(p.splits) + " K slice(s)";
+    return p;
+}
+
+static void set_tile(Plan& p, int cfg, int64_t M, int64_t N) {
+    const TileShape t = tile_shape(cfg);
+    p.tile_cfg = cfg;
+    p.bm = t.bm;
+    p.bn = t.bn;
+    p.bk = t.bk;
+    p.threads = t.threads;
+    p.tiles_m = cdiv(M, t.bm);
+    p.tiles_n = cdiv(N, t.bn);
+    p.tiles = p.tiles_m * p.tiles_n;
+}
+
+static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+    Plan p;
+    p.kernel = kKernTile;
+    p.nxcd = dev.nxcd;
+    const int64_t kt_total = cdiv(K, 64);
+    set_tile(p, kTile256x256w4, M, N);
+    if (p.tiles >= dev.cus) {
+        p.reason = "256x256 tiles fill at least one wave";
+    } else {
+        set_tile(p, kTile128x128w4, M, N);
+        p.reason = "256x256 grid below one wave: 128x128 tiles";
+    }
+    p.group_m = (int)std::min<int64_t>(4, p.tiles_m);
+    p.sched = kSchedDataParallel;
+    p.splits = 1;
+    p.kt_per_split = (int)kt_total;
+    // 128x128 tiles: LDS 64 KB per workgroup, so two fit on a CU
+    const int per_cu = (p.tile_cfg == kTile128x128w4) ? 2 : 1;
+    p.slots = (int64_t)dev.cus * per_cu;
+    if (p.tiles < p.slots && kt_total > 1) {
+        // split K over the idle slots; pieces are summed in K order by the last arriver
+        int64_t s = std::min<int64_t>(kt_total, std::max<int64_t>(1, p.slots / p.tiles));
+        const int64_t slot_floats = (int64_t)p.bm * p.bn;
+        while (s > 1 && p.tiles * s * slot_floats > dev.ws_floats) --s;
+        if (s > 1 && p.tiles > dev.ws_counters) s = 1;
+        if (s > 1) {
+            p.kt_per_split = (int)cdiv(kt_total, s);
+            p.splits = (int)cdiv(kt_total, p.kt_per_split);
+            if (p.splits > 1) {
+                p.sched = kSchedSplitK;
+                p.ws_floats = p.tiles * p.splits * slot_floats;
+                p.counters = p.tiles;
+                p.reason += ", K split " + std::to_string(p.splits) + " ways";
+            }
+        }
+    }
+    p.grid = p.tiles * (p.sched == kSchedSplitK ? p.splits : 1);
+    finish_waves(p);
+    return p;
+}
+
+Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast_ok, int force) {
+    Plan p;
+    if (M == 0 || N == 0) {
+        p.kernel = kKernNone;
+        p.reason = "empty output";
+        return p;
+    }
+    if (K == 0) {
+        p.kernel = kKernZero;
+        p.grid = 1;
+        p.reason = "K == 0: C is the empty sum";
+        return p;
+    }
+    if (!fast_ok) {
+        p.kernel = kKernGeneric;
+        p.grid = cdiv(M, 64) * cdiv(N, 64);
+        p.threads = 256;
+        p.slots = (int64_t)dev.cus * 4;
+        finish_waves(p);
+        p.reason = "alignment, leading dimension or size outside the fast kernels";
+        return p;
+    }
+    const bool skinny = (force == 1) || (force == 0 && M <= 64);
+    return skinny ? plan_skinny(M, N, K, dev) : plan_tile(M, N, K, dev);
+}
+
+static const char* kernel_name(int k) {
+    switch (k) {
+        case kKernNone: return "none";
+        case kKernZero: return "zero";
+        case kKernGeneric: return "generic";
+        case kKernTile: return "tile";
+        case kKernSkinny: return "skinny";
+        default: return "?";
+    }
+}
+
+std::string plan_json(const Plan& p, int64_t M, int64_t N, int64_t K) {
+    char buf[1024];
+    snprintf(buf, sizeof buf,
+             "{\"M\": %lld, \"N\": %lld, \"K\": %lld, \"kernel\": \"%s\", \"bm\": %d, \"bn\": %d, "
+             "\"bk\": %d, \"threads\": %d, \"tiles_m\": %lld, \"tiles_n\": %lld, \"tiles\": %lld, "
+             "\"schedule\": \"%s\", \"splits\": %d, \"kt_per_split\": %d, \"group_m\": %d, "
+             "\"nxcd\": %d, \"mtiles\": %d, \"strips\": %d, \"kb_per_split\": %d, \"grid\": %lld, "
+             "\"slots\": %lld, \"waves\": %lld, \"wave_eff\": %.6f, \"ws_floats\": %lld, "
+             "\"reason\": \"%s\"}",
+             (long long)M, (long long)N, (long long)K, kernel_name(p.kernel), p.bm, p.bn, p.bk,
+             p.threads, (long long)p.tiles_m, (long long)p.tiles_n, (long long)p.tiles,
+             p.kernel == kKernTile ? (p.sched == kSchedSplitK ? "split-k" : "data-parallel")
+                                   : (p.kernel == kKernSkinny ? "strips" : "-"),
+             p.splits, p.kt_per_split, p.group_m, p.nxcd, p.mtiles, p.strips, p.kb_per_split,
+             (long long)p.grid, (long long)p.slots, (long long)p.waves, p.wave_eff,
+             (long long)p.ws_floats, p.reason.c_str());
+    return std::string(buf);
+}
+
+}  // namespace glk

@@ -1,0 +1,162 @@
+/*
+ * gemm_bf16.h: C ABI of the MI355X (gfx950) bf16 matrix-multiply library.
+ *
+ * The library computes C = A * B with bf16 inputs, float32 accumulation and bf16 output
+ * (rounded to nearest, ties to even). This is the product the spark-kernels post builds up in
+ * "the bf16 gemm" (a 4096^3 GEMM in bf16 with fp32 accumulation, then the Llama-7B MLP shapes
+ * and decode shapes) and that "The kernels that were there" specialises in "The GEMV" for
+ * M = 1 or 2 (fp32 accumulate, bf16 store).
+ *
+ * Layout (all row-major, element type bf16 = 16-bit bfloat16 bit patterns):
+ *   A  M x K, element (i, k) at A[i * lda + k], lda >= K
+ *   B  K x N, element (k, j) at B[k * ldb + j], ldb >= N
+ *   C  M x N, element (i, j) at C[i * ldc + j], ldc >= N, fully overwritten (no alpha/beta)
+ * A, B and C are device pointers owned by the caller; the library never allocates, frees or
+ * retains them. C must not overlap A or B.
+ *
+ * Every function is extern "C", returns an int status (gemm_status_t) and never throws.
+ * Argument errors are detected on the host before any HIP call, so they are reported even on
+ * a machine without a GPU. Compute calls only enqueue work on the caller's stream (never the
+ * null stream unless the caller passes it) and return without synchronising; this is what lets
+ * a caller capture them into a graph ("The kernels that were there", "The bench that lied":
+ * the launch has to go to the stream being captured).
+ */
+#ifndef GEMM_BF16_H
+#define GEMM_BF16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *gemm_stream_t; /* the same type as hipStream_t */
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = 1,     /* bad dimension, leading dimension, null pointer */
+    GEMM_ERR_UNSUPPORTED = 2,     /* e.g. M > 64 on the skinny entry point */
+    GEMM_ERR_NOT_INITIALIZED = 3, /* compute call before gemm_init on this device */
+    GEMM_ERR_HIP = 4              /* a HIP runtime call or kernel launch failed */
+} gemm_status_t;
+
+/*
+ * gemm_init: prepare the library for HIP device `device` (queries the device's compute-unit
+ * count and LDS size for the planner, and allocates the library-owned workspace used by split
+ * tiles: float32 partial slots plus counters, zeroed once here and returned to zero by the
+ * kernels that use them, so no call ever needs a memset). Call it outside graph capture, before
+ * the first compute call on that device. Calling it again for an initialised device is a no-op.
+ * Returns GEMM_ERR_HIP when the device cannot be used.
+ */
+int gemm_init(int device);
+
+/*
+ * gemm_bf16: C = A * B (bf16 in, float32 accumulate, bf16 out, round to nearest even).
+ * Dispatch: M <= 64 runs the skinny weight-streaming kernel (the decode shapes of the
+ * spark-kernels post, "the decode kernel"); larger M runs the large-tile MFMA kernel with a tile
+ * and schedule chosen per call from the shape and the device's compute-unit count ("1024 cubed
+ * and the decode shapes": the launch picks the tile per call). Operands whose pointers are not
+ * 16-byte aligned, or whose N, K, lda, ldb, ldc are not multiples of 8, take a general kernel
+ * with the same result contract.
+ * M == 0 or N == 0: nothing is launched. K == 0: C is set to zero (the empty sum).
+ * Errors: GEMM_ERR_INVALID_ARG for negative sizes, lda < K, ldb < N, ldc < N, or a null
+ * pointer with a non-empty extent; GEMM_ERR_NOT_INITIALIZED before gemm_init; GEMM_ERR_HIP if a
+ * launch fails. The call is deterministic: the same inputs give the same bits on every run.
+ * Two calls that run concurrently on different streams of one device share the workspace and
+ * must be serialised by the caller.
+ */
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const void *A, int64_t lda,
+              const void *B, int64_t ldb,
+              void *C, int64_t ldc,
+              gemm_stream_t stream);
+
+/*
+ * gemm_bf16_skinny: the same product, forced onto the skinny kernel: every byte of B is read
+ * once for all M rows ("The kernels that were there", "The GEMV": the M = 2 kernel loads each
+ * weight once for both rows; spark-kernels "the decode kernel"). Requires 1 <= M <= 64
+ * (GEMM_ERR_UNSUPPORTED otherwise); same layout, errors and semantics as gemm_bf16.
+ */
+int gemm_bf16_skinny(int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda,
+                     const void *B, int64_t ldb,
+                     void *C, int64_t ldc,
+                     gemm_stream_t stream);
+
+/*
+ * gemm_bf16_tiled: the same product, forced onto the large-tile MFMA kernel family (any M >= 1),
+ * for comparisons and tests. Same layout, errors and semantics as gemm_bf16.
+ */
+int gemm_bf16_tiled(int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda,
+                    const void *B, int64_t ldb,
+                    void *C, int64_t ldc,
+                    gemm_stream_t stream);
+
+/*
+ * gemm_plan_describe: host-only. Writes, as a JSON object, the plan the library would use for an
+ * M x N x K product on a device with `cus` compute units (tile, grid, schedule, split count,
+ * wave count and wave efficiency = (tiles/slots)/ceil(tiles/slots), the quantity of "Kernel
+ * development on sm_120", section 4, budget 4). `skinny` selects the skinny entry point's plan.
+ * Touches no HIP state. Returns GEMM_ERR_INVALID_ARG for bad sizes or a buffer too small
+ * (buf is always NUL-terminated when len > 0).
+ */
+int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int skinny, char *buf, int len);
+
+/*
+ * gemm_wave_efficiency: host-only closed form of "Kernel development on sm_120", section 4,
+ * budget 4: with `ctas` workgroups over `slots` concurrent slots,
+ * (ctas / slots) / ceil(ctas / slots). Writes the efficiency and the wave count.
+ */
+int gemm_wave_efficiency(int64_t ctas, int64_t slots, double *efficiency, int64_t *waves);
+
+/* gemm_last_plan: the JSON plan of the last successful compute call (any device) into buf. */
+int gemm_last_plan(char *buf, int len);
+
+/* gemm_status_string: a static, human-readable name for a status code. */
+const char *gemm_status_string(int status);
+
+/* gemm_finalize: release the workspaces of every initialised device (call outside capture,
+ * after the caller's streams have drained). */
+int gemm_finalize(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Measurement kernels: the card's own roofs, measured rather than quoted (spark-kernels post,
+ * "how things are measured": a loop of register-resident matrix instructions and a device copy;
+ * "the decode kernel": a read-only kernel with 16-byte loads, an empty launch, single launch vs
+ * back to back; "Kernel development on sm_120", section 1: measure peak DRAM bandwidth and peak
+ * matmul rate, never derive them). All enqueue on `stream` and return immediately.
+ * ------------------------------------------------------------------------------------------ */
+
+/*
+ * gemm_peak_mfma_launch: `blocks` workgroups of 256 threads each run `iters` iterations of
+ * 8 independent v_mfma_f32_32x32x16_bf16 chains on register-resident operands per wave
+ * (16 * 32^3 flops per instruction; flops = blocks * 4 waves * iters * 8 * 32768).
+ * `sink` (device, >= blocks * 256 floats) receives a reduction of the accumulators so the work
+ * cannot be removed; `cycles` (device, >= 2 * blocks uint64) receives, per block, the
+ * s_memtime delta (shader clock cycles) and the s_memrealtime delta (100 MHz constant clock)
+ * measured by wave 0 around its loop.
+ */
+int gemm_peak_mfma_launch(int64_t iters, int blocks, float *sink, uint64_t *cycles,
+                          gemm_stream_t stream);
+
+/* gemm_peak_copy_launch: dst[0 .. bytes) = src[0 .. bytes) with 16-byte loads and stores;
+ * bytes must be a multiple of 16 and both pointers 16-byte aligned. HBM traffic = 2 * bytes. */
+int gemm_peak_copy_launch(const void *src, void *dst, int64_t bytes, gemm_stream_t stream);
+
+/* gemm_peak_read_launch: reads src[0 .. bytes) with 16-byte loads and writes one 32-bit value
+ * per workgroup to sink (device, >= 65536 uint32) so the loads are kept. bytes % 16 == 0. */
+int gemm_peak_read_launch(const void *src, int64_t bytes, uint32_t *sink, gemm_stream_t stream);
+
+/* gemm_peak_empty_launch: one workgroup that does nothing (launch floor). */
+int gemm_peak_empty_launch(gemm_stream_t stream);
+
+/* gemm_fill_launch: writes the 32-bit `value` over dst[0 .. bytes) (bytes % 4 == 0); used to
+ * evict the device's caches between timed calls and to poison outputs before checks. */
+int gemm_fill_launch(void *dst, int64_t bytes, uint32_t value, gemm_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_BF16_H */

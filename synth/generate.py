@@ -2,12 +2,15 @@
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
-_CHUNK = 1 << 22  # elements generated per numpy pass, bounds temporary memory
+_CHUNK = 1 << 20  # elements generated per numpy pass, bounds temporary memory
 
 
 def splitmix64(seed: int, counters: np.ndarray) -> np.ndarray:
@@ -48,26 +51,43 @@ def _normal_chunk(seed: int, start: int, count: int, sigma: float) -> np.ndarray
     return f32_to_bf16_bits((z * sigma).astype(np.float32))
 
 
+def _threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _chunked(count: int, fill) -> np.ndarray:
+    """Run fill(offset, n) -> array over fixed chunks, in parallel threads (numpy drops the GIL)."""
+    out = np.empty(count, dtype=np.uint16)
+    starts = list(range(0, count, _CHUNK))
+
+    def work(s):
+        n = min(_CHUNK, count - s)
+        out[s:s + n] = fill(s, n)
+
+    if len(starts) <= 1:
+        for s in starts:
+            work(s)
+    else:
+        with ThreadPoolExecutor(max_workers=_threads()) as ex:
+            list(ex.map(work, starts))
+    return out
+
+
 def normal_bf16(seed: int, count: int, sigma: float = 1.0, start: int = 0) -> np.ndarray:
     """``count`` bf16 samples of N(0, sigma^2), elements ``start .. start+count-1`` of stream ``seed``."""
-    out = np.empty(count, dtype=np.uint16)
-    for s in range(0, count, _CHUNK):
-        n = min(_CHUNK, count - s)
-        out[s:s + n] = _normal_chunk(seed, start + s, n, sigma)
-    return out
+    return _chunked(count, lambda s, n: _normal_chunk(seed, start + s, n, sigma))
 
 
 def integer_bf16(seed: int, count: int, radius: int = 4, start: int = 0) -> np.ndarray:
     """``count`` integers uniform-ish in [-radius, radius], as exact bf16 bit patterns."""
     if not (0 <= radius <= 128):
         raise ValueError("radius must be in [0, 128] so every value is exact in bf16")
-    out = np.empty(count, dtype=np.uint16)
-    for s in range(0, count, _CHUNK):
-        n = min(_CHUNK, count - s)
+    def fill(s, n):
         idx = np.arange(start + s, start + s + n, dtype=np.uint64)
         v = (splitmix64(seed, idx) >> np.uint64(32)) % np.uint64(2 * radius + 1)
-        out[s:s + n] = f32_to_bf16_bits(v.astype(np.float32) - np.float32(radius))
-    return out
+        return f32_to_bf16_bits(v.astype(np.float32) - np.float32(radius))
+
+    return _chunked(count, fill)
 
 
 def ones_bf16(count: int) -> np.ndarray:

@@ -1,0 +1,78 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before touching HIP."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemv_layers_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gemm_bf16.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = g.lib()
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(g.EXPORTS) == names
+
+
+def test_status_strings():
+    assert g.status_string(0) == "GEMM_OK"
+    assert g.status_string(2) == "GEMM_ERR_UNSUPPORTED"
+    assert g.status_string(99) == "GEMM_ERR_UNKNOWN"
+
+
+P = ctypes.c_void_p(16)  # a non-null, 16-byte aligned stand-in; never dereferenced here
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 8, 8, P, 8, P, 8, P, 8), g.GEMM_ERR_INVALID_ARG),
+    ((8, -1, 8, P, 8, P, 8, P, 8), g.GEMM_ERR_INVALID_ARG),
+    ((8, 8, -1, P, 8, P, 8, P, 8), g.GEMM_ERR_INVALID_ARG),
+    ((8, 8, 16, P, 8, P, 8, P, 8), g.GEMM_ERR_INVALID_ARG),      # lda < K
+    ((8, 16, 8, P, 8, P, 8, P, 16), g.GEMM_ERR_INVALID_ARG),     # ldb < N
+    ((8, 16, 8, P, 8, P, 16, P, 8), g.GEMM_ERR_INVALID_ARG),     # ldc < N
+    ((8, 8, 8, None, 8, P, 8, P, 8), g.GEMM_ERR_INVALID_ARG),    # null A
+    ((8, 8, 8, P, 8, None, 8, P, 8), g.GEMM_ERR_INVALID_ARG),    # null B
+    ((8, 8, 8, P, 8, P, 8, None, 8), g.GEMM_ERR_INVALID_ARG),    # null C
+    ((0, 8, 8, None, 8, P, 8, None, 8), g.GEMM_OK),              # empty output: no-op
+    ((8, 0, 8, P, 8, None, 8, None, 8), g.GEMM_OK),
+    ((0, 8, 8, None, 8, None, 8, None, 8), g.GEMM_ERR_INVALID_ARG),  # B (8 x 8) null
+    ((8, 8, 8, P, 8, P, 8, P, 8), g.GEMM_ERR_NOT_INITIALIZED),   # no gemm_init yet
+])
+def test_validation_without_gpu(args, status):
+    assert g.lib().gemm_bf16(*args, None) == status
+
+
+def test_skinny_entry_rejects_large_m():
+    L = g.lib()
+    assert L.gemm_bf16_skinny(65, 8, 8, P, 8, P, 8, P, 8, None) == g.GEMM_ERR_UNSUPPORTED
+    assert L.gemm_bf16_skinny(0, 8, 8, P, 8, P, 8, P, 8, None) == g.GEMM_ERR_UNSUPPORTED
+    assert L.gemm_bf16_skinny(64, 8, 8, P, 8, P, 8, P, 8, None) == g.GEMM_ERR_NOT_INITIALIZED
+
+
+def test_measurement_entry_validation():
+    L = g.lib()
+    assert L.gemm_peak_copy_launch(P, P, 17, None) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_peak_copy_launch(P, ctypes.c_void_p(8), 16, None) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_peak_copy_launch(P, P, 0, None) == g.GEMM_OK
+    assert L.gemm_peak_read_launch(P, 16, None, None) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_fill_launch(P, 6, 0, None) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_peak_mfma_launch(10, 0, P, P, None) == g.GEMM_ERR_INVALID_ARG
+
+
+def test_last_plan_buffer_handling():
+    buf = ctypes.create_string_buffer(2)
+    assert g.lib().gemm_last_plan(buf, 2) in (g.GEMM_OK, g.GEMM_ERR_INVALID_ARG)
+    assert g.lib().gemm_last_plan(None, 0) == g.GEMM_ERR_INVALID_ARG

@@ -1,0 +1,295 @@
+"""Parity of the HIP path with the float64 oracle, through the C ABI, on an MI355X.
+
+Every product is checked element by element: for floating inputs against
+|c - ref| <= 2^-8 |ref| + 2^-16 sum|a b| and a relative Frobenius error <= 4e-3 (the oracle's
+check); for integer-valued inputs (all partial sums exact in float32) bit for bit against the
+oracle's round-to-nearest-even of the exact result. Outputs are poisoned with NaN before each
+call so a skipped tile cannot pass on stale data. Full-size workloads run in the launch
+configuration the benchmark times (the dispatching entry point) and are compared on sampled
+rows, plus closed-form properties (all-ones gives K everywhere) over every element.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import WORKLOADS, matrix
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import gemv_layers_amd as g  # noqa: E402
+
+POISON = 0x7FC07FC0  # two bf16 quiet NaNs
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    torch.cuda.set_device(0)
+    g.gemm_init(0)
+    yield
+
+
+def dev(h: np.ndarray) -> "torch.Tensor":
+    t = torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).view(torch.bfloat16)
+    return t.to("cuda")
+
+
+def host(t: "torch.Tensor") -> np.ndarray:
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+ENTRIES = {"auto": g.gemm_bf16, "tiled": g.gemm_bf16_tiled, "skinny": g.gemm_bf16_skinny}
+
+
+def run(entry, A, B, M, N, K, ldc=None, C=None):
+    """Call the library on host bf16-bit arrays A (M x lda) and B (K x ldb); returns C bits."""
+    ldc = N if ldc is None else ldc
+    dA, dB = dev(A), dev(B)
+    if C is None:
+        n = -(-max(M * ldc, 8) // 8) * 8      # whole 16-byte units for the poison fill
+        C = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        g.gemm_fill_launch(ctypes.c_void_p(C.data_ptr()), C.numel() * 2, POISON)
+    s = g.current_stream_handle()
+    ENTRIES[entry](M, N, K, ctypes.c_void_p(dA.data_ptr()), A.shape[1] if A.size else max(K, 1),
+                   ctypes.c_void_p(dB.data_ptr()), B.shape[1] if B.size else max(N, 1),
+                   ctypes.c_void_p(C.data_ptr()), ldc, s)
+    torch.cuda.synchronize()
+    return host(C)[: M * ldc].reshape(M, ldc)[:, :N]
+
+
+def check_float(C, A, B, M, N, K, what=""):
+    ref, sabs = oracle.gemm(A, B, M=M, N=N, K=K)
+    res = oracle.check(C, ref, sabs)
+    assert res.ok, f"{what} {res.summary()}"
+    return res
+
+
+def check_exact(C, A, B, M, N, K, what=""):
+    ref, _ = oracle.gemm(A, B, M=M, N=N, K=K, with_abs=False)
+    want = oracle.bf16_rne(ref)
+    bad = np.argwhere(C != want)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[0].tolist()}"
+
+
+# ---- small and ragged shapes, each kernel family --------------------------------------------
+
+TILE_SHAPES = [(256, 256, 64), (512, 512, 512), (300, 520, 328), (1000, 1000, 1000),
+               (65, 264, 72), (1, 8, 8), (257, 264, 4104), (513, 1032, 136)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+def test_tile_kernel_float_and_exact(M, N, K):
+    A = matrix("normal", M, K, seed=1000 + M)
+    B = matrix("normal", K, N, seed=2000 + N, sigma=0.5)
+    check_float(run("tiled", A, B, M, N, K), A, B, M, N, K, f"tiled {M}x{N}x{K}")
+    Ai = matrix("int", M, K, seed=3000 + M)
+    Bi = matrix("int", K, N, seed=4000 + N)
+    check_exact(run("tiled", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"tiled int {M}x{N}x{K}")
+
+
+SKINNY_SHAPES = [(m, n, k) for m in (1, 2, 3, 16, 17, 33, 64)
+                 for (n, k) in ((1000, 1000), (264, 4104), (4104, 320))]
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)
+def test_skinny_kernel_float_and_exact(M, N, K):
+    A = matrix("normal", M, K, seed=5000 + M)
+    B = matrix("normal", K, N, seed=6000 + N, sigma=0.02)
+    check_float(run("skinny", A, B, M, N, K), A, B, M, N, K, f"skinny {M}x{N}x{K}")
+    Ai = matrix("int", M, K, seed=7000 + M)
+    Bi = matrix("int", K, N, seed=8000 + N)
+    check_exact(run("skinny", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"skinny int {M}x{N}x{K}")
+
+
+GENERIC_SHAPES = [(17, 15, 63), (5, 33, 1), (70, 9, 100), (1, 1, 1), (130, 67, 255)]
+
+
+@pytest.mark.parametrize("M,N,K", GENERIC_SHAPES)
+def test_general_kernel_odd_shapes(M, N, K):
+    A = matrix("normal", M, K, seed=9000 + M)
+    B = matrix("normal", K, N, seed=9100 + N)
+    C = run("auto", A, B, M, N, K)
+    assert g.gemm_last_plan()["kernel"] == "generic"
+    check_float(C, A, B, M, N, K, f"generic {M}x{N}x{K}")
+    Ai, Bi = matrix("int", M, K, seed=9200), matrix("int", K, N, seed=9300)
+    check_exact(run("auto", Ai, Bi, M, N, K), Ai, Bi, M, N, K)
+
+
+@pytest.mark.parametrize("entry", ["tiled", "skinny", "auto"])
+def test_leading_dimensions_never_read_padding(entry):
+    # padding columns hold NaN: a kernel that reads them produces NaN and fails
+    M, N, K = (48, 264, 200) if entry != "tiled" else (300, 264, 200)
+    A = matrix("normal", M, K, seed=11, ld=K + 24)
+    B = matrix("normal", K, N, seed=12, ld=N + 16)
+    C = run(entry, A, B, M, N, K, ldc=N + 8)
+    ref, sabs = oracle.gemm(A, B, M=M, N=N, K=K)
+    assert oracle.check(C, ref, sabs).ok
+
+
+def test_dispatch_on_m():
+    A64, A65 = matrix("int", 64, 512, seed=1), matrix("int", 65, 512, seed=1)
+    B = matrix("int", 512, 1024, seed=2)
+    check_exact(run("auto", A64, B, 64, 1024, 512), A64, B, 64, 1024, 512)
+    assert g.gemm_last_plan()["kernel"] == "skinny"
+    check_exact(run("auto", A65, B, 65, 1024, 512), A65, B, 65, 1024, 512)
+    assert g.gemm_last_plan()["kernel"] == "tile"
+
+
+def test_degenerate_shapes():
+    A = np.zeros((8, 8), np.uint16)
+    B = np.zeros((8, 16), np.uint16)
+    C = run("auto", A, B, 8, 16, 0)             # K = 0: the empty sum
+    assert np.all(C == 0)
+    Cd = torch.empty(64, dtype=torch.bfloat16, device="cuda")
+    g.gemm_fill_launch(ctypes.c_void_p(Cd.data_ptr()), 128, POISON)
+    dA, dB = dev(A), dev(B)
+    g.gemm_bf16(0, 16, 8, ctypes.c_void_p(dA.data_ptr()), 8, ctypes.c_void_p(dB.data_ptr()), 16,
+                ctypes.c_void_p(Cd.data_ptr()), 16, g.current_stream_handle())
+    torch.cuda.synchronize()
+    assert np.all(host(Cd) == 0x7FC0)           # M = 0: nothing written
+
+
+def _rne_golden():
+    import os
+    rows = []
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "rne_ties.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            x, bits = line.split()[:2]
+            rows.append((float(x), int(bits, 16)))
+    return rows
+
+
+@pytest.mark.parametrize("entry,M", [("tiled", 256), ("skinny", 16), ("auto", 5)])
+def test_epilogue_rounds_to_nearest_even(entry, M):
+    # c = a0*b0 + a1*b1 with a = [1, 1]: b0 = 4096, b1 = x - 4096 gives the golden tie cases
+    ties = [(x, b) for x, b in _rne_golden() if 4096 <= abs(x) <= 4160]
+    N, K = 264, 64
+    A = np.zeros((M, K), np.uint16)
+    A[:, 0] = 0x3F80
+    A[:, 1] = 0x3F80
+    B = np.zeros((K, N), np.uint16)
+    want = np.zeros(N, np.uint16)
+    for j in range(N):
+        x, bits = ties[j % len(ties)]
+        sgn = -1.0 if x < 0 else 1.0
+        B[0, j] = oracle.bf16_rne(sgn * 4096.0)
+        B[1, j] = oracle.bf16_rne(x - sgn * 4096.0)
+        want[j] = bits
+    C = run(entry, A, B, M, N, K)
+    assert np.all(C == want[None, :])
+
+
+# ---- full-size workloads, in the benchmark's launch configuration -------------------------
+
+FULL = ["sq512", "sq4096", "sq8192", "sq16384", "mlp_up", "mlp_down"] + \
+       [n for n in WORKLOADS if n.startswith("dec_")]
+
+
+def _sample_rows(M, n):
+    if M <= n:
+        return np.arange(M)
+    rng = np.random.default_rng(M)
+    return np.unique(np.concatenate([[0, M - 1, M // 2], rng.choice(M, n - 3, replace=False)]))
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full_size(name):
+    w = WORKLOADS[name]
+    A = matrix("normal", w.M, w.K, seed=w.seed_a, sigma=w.sigma_a)
+    B = matrix("normal", w.K, w.N, seed=w.seed_b, sigma=w.sigma_b)
+    C = run("auto", A, B, w.M, w.N, w.K)
+    rows = _sample_rows(w.M, 64 if w.M <= 4096 else 24)
+    As = np.ascontiguousarray(A[rows])
+    ref, sabs = oracle.gemm(As, B, M=len(rows), N=w.N, K=w.K)
+    res = oracle.check(np.ascontiguousarray(C[rows]), ref, sabs)
+    assert res.ok, f"{name} rows={len(rows)} {res.summary()}"
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_all_ones_every_element(name):
+    w = WORKLOADS[name]
+    A = np.full((w.M, w.K), 0x3F80, np.uint16)
+    B = np.full((w.K, w.N), 0x3F80, np.uint16)
+    C = run("auto", A, B, w.M, w.N, w.K)
+    want = oracle.bf16_rne(float(w.K))
+    bad = np.count_nonzero(C != want)
+    assert bad == 0, f"{name}: {bad} elements differ from K = {w.K}"
+
+
+@pytest.mark.parametrize("name", ["sq4096", "mlp_up", "mlp_down", "dec_up_M64", "dec_down_M16"])
+def test_workload_integer_exact_sampled(name):
+    w = WORKLOADS[name]
+    A = matrix("int", w.M, w.K, seed=w.seed_a)
+    B = matrix("int", w.K, w.N, seed=w.seed_b)
+    C = run("auto", A, B, w.M, w.N, w.K)
+    rows = _sample_rows(w.M, 32)
+    ref, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, M=len(rows), N=w.N, K=w.K,
+                         with_abs=False)
+    want = oracle.bf16_rne(ref)
+    bad = np.argwhere(C[rows] != want)
+    assert bad.size == 0, f"{name}: {len(bad)} mismatches, first {bad[0].tolist()}"
+
+
+# ---- determinism and workspace hygiene -------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["sq4096", "sq512", "dec_down_M64", "dec_up_M1"])
+def test_bitwise_deterministic_and_workspace_clean(name):
+    w = WORKLOADS[name]
+    A = matrix("normal", w.M, w.K, seed=w.seed_a, sigma=w.sigma_a)
+    B = matrix("normal", w.K, w.N, seed=w.seed_b, sigma=w.sigma_b)
+    first = run("auto", A, B, w.M, w.N, w.K)
+    # interleave other shapes that use the same workspace, then repeat
+    other = matrix("normal", 3, 1000, seed=5)
+    ob = matrix("normal", 1000, 4104, seed=6)
+    for _ in range(3):
+        run("skinny", other, ob, 3, 4104, 1000)
+        again = run("auto", A, B, w.M, w.N, w.K)
+        assert np.array_equal(first, again), name
+
+
+def test_many_back_to_back_calls_stay_correct():
+    # 200 launches on one stream with no synchronisation in between; the split-K counters must
+    # return to zero every time or later calls would lose their fixup
+    M, N, K = 16, 4096, 11008
+    A = matrix("int", M, K, seed=1)
+    B = matrix("int", K, N, seed=2)
+    dA, dB = dev(A), dev(B)
+    outs = [torch.empty(M * N, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    s = g.current_stream_handle()
+    for i in range(200):
+        C = outs[i % 4]
+        g.gemm_fill_launch(ctypes.c_void_p(C.data_ptr()), C.numel() * 2, POISON, s)
+        g.gemm_bf16(M, N, K, ctypes.c_void_p(dA.data_ptr()), K, ctypes.c_void_p(dB.data_ptr()), N,
+                    ctypes.c_void_p(C.data_ptr()), N, s)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm(A, B, with_abs=False)
+    want = oracle.bf16_rne(ref)
+    for C in outs:
+        assert np.array_equal(host(C).reshape(M, N), want)
+
+
+# ---- measurement kernels ---------------------------------------------------------------------
+
+def test_measurement_kernels_run_and_copy_is_exact():
+    n = 64 << 20
+    src = torch.randint(-2**31, 2**31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    s = g.current_stream_handle()
+    g.gemm_peak_copy_launch(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, s)
+    sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+    g.gemm_peak_read_launch(ctypes.c_void_p(src.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()), s)
+    g.gemm_peak_empty_launch(s)
+    blocks = 256
+    fs = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    g.gemm_peak_mfma_launch(1000, blocks, ctypes.c_void_p(fs.data_ptr()),
+                            ctypes.c_void_p(cyc.data_ptr()), s)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    assert torch.all(cyc > 0)
+    assert torch.isfinite(fs).all()

@@ -1,0 +1,88 @@
+"""The host planner: page-printed wave figures, and the plans at the workload shapes on 256 CUs."""
+
+import math
+import os
+
+import pytest
+
+import gemv_layers_amd as g
+from synth import WORKLOADS
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _fixtures():
+    out = []
+    for line in open(os.path.join(GOLDEN, "planner_fixtures.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            c, s, w, e, tol = line.split()[:5]
+            out.append((int(c), int(s), int(w), float(e), float(tol)))
+    return out
+
+
+@pytest.mark.parametrize("ctas,slots,waves,eff,tol", _fixtures())
+def test_wave_efficiency_matches_printed_figures(ctas, slots, waves, eff, tol):
+    e, w = g.gemm_wave_efficiency(ctas, slots)
+    assert w == waves
+    assert abs(e - eff) <= tol
+
+
+def test_two_factor_decomposition_of_printed_example():
+    # "Kernel development on sm_120", section 4: 82.4% of the ceiling = 86.1% waves x 95.7% pipe
+    e, _ = g.gemm_wave_efficiency(1024, 170)
+    assert abs(e - 0.861) < 0.001
+    assert abs(e * 0.957 - 0.824) < 0.001
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("name", ["sq4096", "sq8192", "sq16384", "mlp_up", "mlp_down"])
+def test_large_shapes_use_256_tiles(name):
+    w = WORKLOADS[name]
+    p = g.gemm_plan_describe(w.M, w.N, w.K, 256)
+    assert p["kernel"] == "tile" and (p["bm"], p["bn"]) == (256, 256)
+    tiles = _cdiv(w.M, 256) * _cdiv(w.N, 256)
+    assert p["tiles"] == tiles and p["grid"] == tiles
+    e, waves = g.gemm_wave_efficiency(tiles, 256)
+    assert p["waves"] == waves and abs(p["wave_eff"] - e) < 1e-6
+
+
+def test_mlp_up_wave_quantization():
+    p = g.gemm_plan_describe(4096, 11008, 4096, 256)
+    assert p["tiles"] == 688 and p["waves"] == 3
+    assert abs(p["wave_eff"] - 688 / 768) < 1e-6
+
+
+def test_small_square_splits_k():
+    p = g.gemm_plan_describe(512, 512, 512, 256)
+    assert p["kernel"] == "tile" and (p["bm"], p["bn"]) == (128, 128)
+    assert p["schedule"] == "split-k" and p["splits"] > 1
+    assert p["splits"] * p["kt_per_split"] >= 512 // 64
+    assert (p["splits"] - 1) * p["kt_per_split"] < 512 // 64  # no empty piece
+
+
+@pytest.mark.parametrize("name", [n for n in WORKLOADS if n.startswith("dec_")])
+def test_decode_shapes_stream_weights(name):
+    w = WORKLOADS[name]
+    p = g.gemm_plan_describe(w.M, w.N, w.K, 256)
+    assert p["kernel"] == "skinny"
+    assert p["mtiles"] == _cdiv(w.M, 16)
+    assert p["strips"] == _cdiv(w.N, 128)
+    kblocks = _cdiv(w.K, 32)
+    assert p["splits"] * p["kb_per_split"] >= kblocks
+    assert (p["splits"] - 1) * p["kb_per_split"] < kblocks
+    assert p["grid"] == p["strips"] * p["splits"]
+    assert p["grid"] >= 256  # enough workgroups to cover every CU
+
+
+def test_dispatch_threshold_and_degenerate():
+    assert g.gemm_plan_describe(64, 4096, 4096, 256)["kernel"] == "skinny"
+    assert g.gemm_plan_describe(65, 4096, 4096, 256)["kernel"] == "tile"
+    assert g.gemm_plan_describe(65, 4096, 4096, 256, skinny=False)["kernel"] == "tile"
+    assert g.gemm_plan_describe(0, 8, 8, 256)["kernel"] == "none"
+    assert g.gemm_plan_describe(8, 8, 0, 256)["kernel"] == "zero"
+    with pytest.raises(g.GemmError):
+        g.gemm_plan_describe(65, 8, 8, 256, skinny=True)
