@@ -3,12 +3,13 @@
 
 #include <hip/hip_runtime.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
 #include <string>
 
-#include "../../include/gemm_bf16.h"
+#include "gemm_bf16.h"
 #include "kernels.h"
 #include "plan.h"
 
@@ -117,8 +118,8 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
             s.ldb = (int)ldb;
             s.ldc = (int)ldc;
             s.strips = p.strips;
-            s.splits = p.splits;
-            s.kb_per_split = p.kb_per_split;
+            s.ks = p.ks;
+            s.grid = (int)p.grid;
             s.ws = ds.ws;
             s.counters = ds.counters;
             e = glk::launch_skinny_gemm(p.mtiles, s, stream);
@@ -158,6 +159,7 @@ int gemm_init(int device) {
         if (ds.info.cus % ds.info.nxcd != 0) ds.info.nxcd = 1;
         ds.info.ws_floats = kWsFloats;
         ds.info.ws_counters = kWsCounters;
+        if (const char* f = getenv("GEMM_BF16_FORCE_TILE")) ds.info.force_tile_cfg = atoi(f);
         if (hipMalloc(&ds.ws, kWsFloats * sizeof(float)) != hipSuccess) rc = GEMM_ERR_HIP;
     }
     if (rc == GEMM_OK && hipMalloc(&ds.counters, kWsCounters * sizeof(uint32_t)) != hipSuccess)

@@ -24,6 +24,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
                                              kBufWord3);
 }
 
+// Descriptor with an explicit byte range: offsets at or beyond `bytes` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+
+// `off` when `valid`, else an out-of-range offset; branch-free so that no control flow (and no
+// conservative wait at a merge point) ends up between a wave's outstanding loads.
+__device__ __forceinline__ uint32_t sel_off(bool valid, uint32_t off) {
+    const uint32_t m = 0u - (uint32_t)valid;
+    return (off & m) | (kBufInvalid & ~m);
+}
+
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
@@ -34,6 +46,84 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t of
 
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+// Cache policy for workspace traffic shared between workgroups on different XCDs: device scope
+// (sc1), so stores are written through to the device coherence point and loads do not hit
+// stale lines in another XCD's L2. Publishing a partial is then: device-scope stores, wait for
+// them to complete, workgroup barrier, one device-scope counter increment. No cache-wide
+// write-back or invalidate is needed.
+constexpr int kAuxDevice = 16;
+
+__device__ __forceinline__ void buf_store16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kAuxDevice);
+}
+
+__device__ __forceinline__ u32x4 buf_load16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxDevice);
+}
+
+// Wait for this wave's outstanding vector-memory operations down to N (gfx9 s_waitcnt encoding,
+// other counters unconstrained). Direct-to-LDS loads count here until their data is in LDS.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait for this wave's outstanding LDS operations.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
+
+// Workgroup barrier for LDS rings fed by direct-to-LDS loads. Unlike __syncthreads() it carries
+// no memory fence, so it does not drain the loads still in flight for later stages; each wave
+// first waits (wait_vmcnt) for exactly the loads the next stage needs and for its own LDS reads.
+// The empty asm statements stop the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    wait_lgkmcnt0();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ uint32_t counter_arrive(uint32_t* c) {
+    return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void counter_reset(uint32_t* c) {
+    __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ u32x4 f4_bits(f32x4 v) { return __builtin_bit_cast(u32x4, v); }
+__device__ __forceinline__ f32x4 bits_f4(u32x4 v) { return __builtin_bit_cast(f32x4, v); }
+
+// ---- direct-to-LDS loads --------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+
+// Raw buffer descriptor words (base, stride 0, `bytes` records, raw word 3) for inline asm.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, kBufWord3};
+}
+
+// Each lane copies 16 bytes from descriptor + voff into LDS at lds_base + 16 * lane, without
+// passing through registers. Issued from inline asm so that the compiler does not treat every
+// later LDS read as possibly depending on it (it would wait for all loads in flight before each
+// read); callers order it explicitly with wait_vmcnt<>() and a barrier. Offsets at or beyond the
+// descriptor's range deliver zeros.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_base, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
 }
 
 // float32 pair -> two bf16 (round to nearest even; gfx950 v_cvt_pk_bf16_f32), low half = lo.

@@ -5,187 +5,309 @@
 // columns, coalesced 128-bit weight loads, fp32 accumulation, every weight loaded once for all
 // rows; spark-kernels post, "the decode kernel": a tile of 16/32/64 rows picked from M, one
 // workgroup per column strip of B, and K split only as far as needed to fill the card, the last
-// slice leaving the workspace as it found it so a call stays one launch):
+// slice leaving the workspace as it found it so a call stays one launch; enough bytes in flight
+// per workgroup to reach the memory floor):
 //
-// * A workgroup owns a strip of 128 columns and one K slice; its 4 waves take the slice's
-//   32-row k-blocks in turn. Each lane loads an 8 x 8 bf16 block of B (8 rows x 16 bytes, the 16
-//   lanes of a row group covering 256 contiguous bytes of a row), two k-blocks ahead of use.
-// * The block is transposed in registers so that column c of the block is the first operand of
-//   v_mfma_f32_16x16x32_bf16 (row i of that operand = column 8*i + c of the strip); the second
-//   operand is 16 rows of A, loaded from L2 as 16 bytes per lane. M is padded to 16 per tile with
-//   zeros (the matrix cores are idle in a memory-bound kernel, so the padding costs no time).
-// * The 4 waves' float32 partials are added in LDS in wave order. With more than one K slice,
-//   each slice writes its strip partial to a workspace slot and bumps a per-strip counter; the
-//   last arriver adds the slices in K order, writes bf16 and resets the counter to zero.
+// * The work is a strip-major list of units (one 64-row stage of one 128-column strip). Exactly one
+//   workgroup per CU takes a balanced, contiguous range of units (the Stream-K decomposition of
+//   the spark-kernels post, "stream-k proper"), so no partial last wave of workgroups exists; only
+//   the first and the last strip a range touches can be partial. The units stream through
+//   an LDS ring of STAGES stages: each is fetched with direct-to-LDS buffer loads (16 bytes per
+//   lane, 1 KB per wave instruction, no registers involved), STAGES - 1 stages ahead of use, and
+//   carries the matching 64 columns of A (M rows) so every wave reads A from LDS.
+// * B sits in LDS row-major (k rows of 256 bytes). The MFMA operand wants 8 consecutive k per
+//   lane for one column, which ds_read_b64_tr_b16 produces directly from row-major data: within
+//   each 16-lane group, lanes 4r .. 4r+3 address row r of a 4 x 16 block and lane j receives
+//   column j. The 32-byte column groups of each row are XOR-swizzled with the row so the rows a
+//   wave reads together fall in different banks.
+// * Each of the 4 waves owns 32 columns (two 16-column MFMA tiles) for all M rows, using
+//   v_mfma_f32_16x16x32_bf16 with B as the first operand: each lane's accumulator then holds 4
+//   consecutive columns of one row of C, stored as one 8-byte bf16 write. M is padded to 16 per
+//   tile with zero rows (A rows past M are fetched as zeros); the matrix cores are otherwise idle
+//   in this memory-bound kernel, so the padding costs nothing.
+// * A strip whose units all fall in one workgroup is written straight to C. Otherwise each piece
+//   writes its float32 partial to the workgroup's slot with device-scope stores and bumps a
+//   per-strip counter; the last arriver loads every piece (all loads issued before any add), adds
+//   them in K order, writes bf16 and returns the counter to zero.
 
 #include "common.h"
 #include "kernels.h"
 
 namespace glk {
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kSkRows = 64;                            // k rows per LDS stage
+constexpr int kSkRowBytes = kSkinnyStrip * 2;          // 256 bytes of B per row
+constexpr int kSkBBytes = kSkRows * kSkRowBytes;       // 16 KB of B per stage
+
+template <int MT>
+struct SkinnyTraits {
+    static constexpr int A_BYTES = 16 * MT * kSkRows * 2;  // A rows (M padded to 16 MT) x 64 k
+    static constexpr int STAGE_BYTES = kSkBBytes + A_BYTES;
+    static constexpr int STAGES = 131072 / STAGE_BYTES;    // ring in 128 KB: one workgroup per CU
+    static constexpr int DUMMY = STAGES * STAGE_BYTES;     // 1 KB sink for padding loads
+    static constexpr int LDS_BYTES = DUMMY + 1024;
+    static constexpr int A_INSTR = A_BYTES / 1024;         // 1 KB load instructions for A per stage
+    static constexpr int A_PER_WAVE = (A_INSTR + 3) / 4;
+    static constexpr int LOADS = 4 + A_PER_WAVE;           // load instructions per wave per stage
+    static constexpr int SLOT_FLOATS = 4 * 2 * MT * 64 * 4; // one piece: 4 waves x 2 tiles x M
+    static_assert(STAGES >= 3, "need at least three stages");
+    static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
+};
+
+// Physical 32-byte column group of logical group u in row r (8 groups of 16 columns per row):
+// the 4 rows a 16-lane group reads, and the groups 8 rows apart, land on different banks.
+__device__ __forceinline__ int b_swz(int u, int r) { return u ^ ((r & 3) | (((r >> 3) & 1) << 2)); }
+
 template <int MT>
 __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
-    constexpr int NR = 32 * MT;           // accumulator floats per lane: [c][mt][r]
-    constexpr int PER_WAVE = NR / 4;      // floats per lane each wave finishes after the LDS sum
-    extern __shared__ float red[];        // [4 waves][NR][64 lanes]
+    using T = SkinnyTraits<MT>;
+    constexpr int STAGES = T::STAGES;
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int strip = (int)blockIdx.x % p.strips;  // neighbouring workgroups read the same rows
-    const int split = (int)blockIdx.x / p.strips;
-    const int n0 = strip * kSkinnyStrip;
-    const int kblocks = (p.K + kSkinnyKBlock - 1) / kSkinnyKBlock;
-    const int kb0 = split * p.kb_per_split;
-    const int kb1 = min(kblocks, kb0 + p.kb_per_split);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // ---- this workgroup's units: [u_begin, u_end) of the strip-major (strip, stage) list -------
+    const int64_t U = (int64_t)p.strips * p.ks;
+    const int w = (int)blockIdx.x;
+    const int64_t u_begin = (int64_t)w * U / p.grid;
+    const int64_t u_end = (int64_t)(w + 1) * U / p.grid;
+    const int nunits = (int)(u_end - u_begin);
+    const int first_strip = (int)(u_begin / p.ks);
 
-    const int g = lane >> 4;    // row group: k rows 8g .. 8g+7 of a k-block
-    const int c16 = lane & 15;  // column octet: strip columns 8*c16 .. +7
-    const bool col_ok = (n0 + 8 * c16) < p.N;
-    const uint32_t b_lane = (uint32_t)(8 * g * p.ldb + 8 * c16) * 2u;
-    const uint32_t ldb_bytes = (uint32_t)p.ldb * 2u;
-    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A);
-    uint32_t a_lane[MT];
-    bool a_ok[MT];
+    // ---- load addressing ---------------------------------------------------------------------
+    // B: wave w fetches rows 16w .. 16w+15 of a stage, 4 rows per instruction; lane l lands at
+    // byte 16 l of the instruction's 1 KB = row 4i + l/16 (of the wave's 16), physical 16-byte
+    // chunk l%16, and fetches the logical chunk the swizzle keeps there (the swizzle is an
+    // involution on the group index). Column validity is checked per unit (the strip varies).
+    uint32_t b_off[4];  // byte offset from (stage row 0, strip column 0)
+    int b_col[4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + c16;
-        a_ok[mt] = m < p.M;
-        a_lane[mt] = (uint32_t)(m * p.lda + 8 * g) * 2u;
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * i + (lane >> 4);
+        const int u = b_swz((lane & 15) >> 1, r);
+        b_col[i] = 16 * u + 8 * (lane & 1);
+        b_off[i] = (uint32_t)(r * p.ldb + b_col[i]) * 2u;
     }
+    // A: instruction j (= wave + 4t) covers A rows 8j .. 8j+7 of the padded M x 64 block;
+    // lane l -> row 8j + l/8, physical chunk l%8 holding logical chunk (l%8) ^ (row & 7).
+    uint32_t a_off[T::A_PER_WAVE];
+    int a_chunk[T::A_PER_WAVE];
+#pragma unroll
+    for (int t = 0; t < T::A_PER_WAVE; ++t) {
+        const int j = wave + 4 * t;
+        const int row = 8 * j + (lane >> 3);
+        a_chunk[t] = (lane & 7) ^ (row & 7);
+        a_off[t] = sel_off(j < T::A_INSTR && row < p.M, (uint32_t)(row * p.lda + 8 * a_chunk[t]) * 2u);
+    }
+    const uint32_t dummy_lds = lds_addr(lds + T::DUMMY);
 
-    f32x4 acc[8][MT];
+    // issue the loads of the workgroup's i-th unit into ring slot i % STAGES (units past the
+    // range read nothing: a zero-length descriptor)
+    auto issue_unit = [&](int i) {
+        char* st = lds + (i % STAGES) * T::STAGE_BYTES;
+        const int64_t u = u_begin + i;
+        const int strip = (int)(u / p.ks);
+        const int k0 = (int)(u - (int64_t)strip * p.ks) * kSkRows;
+        const int n0 = strip * kSkinnyStrip;
+        const int rows = (i < nunits) ? min(kSkRows, p.K - k0) : 0;  // uniform
+        const i32x4 b_rsrc = rsrc_words(p.B + (size_t)k0 * p.ldb + n0, (uint32_t)rows * (uint32_t)p.ldb * 2u);
+        const uint32_t st_lds = lds_addr(st);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+        for (int t = 0; t < 4; ++t)
+            dma16(b_rsrc, st_lds + (16 * wave + 4 * t) * kSkRowBytes, sel_off(n0 + b_col[t] < p.N, b_off[t]));
+        // A columns k0 .. k0 + rows; K % 8 == 0, so a 16-byte chunk is wholly in or out. A wave
+        // without a real A instruction this round (the count need not divide by 4) still issues
+        // one, into a spare kilobyte, so every wave issues the same number of loads per unit and
+        // one vmcnt threshold fits all waves.
+        const i32x4 a_rsrc = rsrc_words(p.A + k0, kBufRecords);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[c][mt] = f32x4{};
-
-    auto load = [&](u32x4 (&b)[8], u32x4 (&a)[MT], int kb) {
-        const bool kb_ok = kb < kb1;
-        const int k0 = kb * kSkinnyKBlock;
-        const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(p.B + (size_t)k0 * p.ldb + n0);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const bool ok = kb_ok && col_ok && (k0 + 8 * g + r) < p.K;
-            b[r] = buf_load16(b_rsrc, ok ? b_lane + (uint32_t)r * ldb_bytes : kBufInvalid);
+        for (int t = 0; t < T::A_PER_WAVE; ++t) {
+            const int j = wave + 4 * t;
+            const bool real = j < T::A_INSTR;
+            const uint32_t off = sel_off(real && 8 * a_chunk[t] < rows, a_off[t]);
+            dma16(a_rsrc, real ? st_lds + kSkBBytes + j * 1024 : dummy_lds, off);
         }
-        const bool ak = kb_ok && (k0 + 8 * g) < p.K;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            a[mt] = buf_load16(a_rsrc, (ak && a_ok[mt]) ? a_lane[mt] + (uint32_t)k0 * 2u : kBufInvalid);
     };
 
-    auto compute = [&](const u32x4 (&b)[8], const u32x4 (&a)[MT]) {
-        u32x4 t[8];
-        transpose8x8_b16(b, t);
+    f32x4 acc[2][MT];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const bf16x8 x = __builtin_bit_cast(bf16x8, t[c]);
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[c][mt] = mfma16(x, __builtin_bit_cast(bf16x8, a[mt]), acc[c][mt]);
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{};
+
+    // fragment addressing: 16-lane group G = lane / 16 holds k rows 8G .. 8G+7 of a 32-row block;
+    // inside the group, lane j addresses row (j / 4) of the 4-row transpose block and the 4
+    // columns 4 (j % 4) .. +3 of the 16-column tile.
+    const int fG = lane >> 4, fj = lane & 15;
+    const int tr_row = 8 * fG + (fj >> 2);
+    const int tr_colb = 8 * (fj & 3);
+    const int a_frow = lane & 15;
+
+    auto compute_unit = [&](int i) {
+        const char* st = lds + (i % STAGES) * T::STAGE_BYTES;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {               // two 32-row blocks per stage
+            bf16x8 bx[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int u = 2 * wave + t;            // the wave's 16-column tile (logical group)
+                i16x4 v[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 32 * kb + tr_row + 4 * h;
+                    const char* addr = st + r * kSkRowBytes + b_swz(u, r) * 32 + tr_colb;
+                    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)addr);
+                }
+                typedef short i16x8 __attribute__((ext_vector_type(8)));
+                const i16x8 x = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+                bx[t] = __builtin_bit_cast(bf16x8, x);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row = 16 * mt + a_frow;
+                const int chunk = (4 * kb + fG) ^ (row & 7);
+                const bf16x8 ay = *reinterpret_cast<const bf16x8*>(st + kSkBBytes + row * 128 + chunk * 16);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc[t][mt] = mfma16(bx[t], ay, acc[t][mt]);
+            }
         }
     };
 
-    {
-        u32x4 b0[8], b1[8], a0[MT], a1[MT];
-        int kb = kb0 + wave;
-        load(b0, a0, kb);
-        load(b1, a1, kb + 4);
-        while (kb < kb1) {
-            compute(b0, a0);
-            load(b0, a0, kb + 8);
-            if (kb + 4 >= kb1) break;
-            compute(b1, a1);
-            load(b1, a1, kb + 12);
-            kb += 8;
+    // lane holds rows m = 16 mt + (lane & 15), columns 4 (lane >> 4) + 0..3 of each 16-column tile
+    auto store_c = [&](int strip) {
+        const int n0 = strip * kSkinnyStrip;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int n = n0 + 32 * wave + 16 * t + 4 * (lane >> 4);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int m = 16 * mt + (lane & 15);
+                if (m < p.M && n < p.N) {
+                    u32x2 v = {pack_bf16x2(acc[t][mt][0], acc[t][mt][1]), pack_bf16x2(acc[t][mt][2], acc[t][mt][3])};
+                    *reinterpret_cast<u32x2*>(p.C + (size_t)m * p.ldc + n) = v;
+                }
+            }
         }
-    }
+    };
 
-    // ---- add the 4 waves' partials in wave order -------------------------------------------
-    float* mine = red + (size_t)wave * NR * 64;
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mine[((c * MT + mt) * 4 + r) * 64 + lane] = acc[c][mt][r];
-    __syncthreads();
-    // wave w finishes register indices [w * PER_WAVE, (w + 1) * PER_WAVE)
-    float part[PER_WAVE];
-#pragma unroll
-    for (int t = 0; t < PER_WAVE; ++t) {
-        const int ri = wave * PER_WAVE + t;
-        float s = red[(0 * NR + ri) * 64 + lane];
-        s += red[(1 * NR + ri) * 64 + lane];
-        s += red[(2 * NR + ri) * 64 + lane];
-        s += red[(3 * NR + ri) * 64 + lane];
-        part[t] = s;
-    }
+    // workspace slot of workgroup w's piece of `strip`: 0 for the strip its range starts in, else 1
+    const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.ws);
+    auto slot_off = [&](int wg, int seg, int t, int mt) {
+        return (uint32_t)((((((wg * 2 + seg) * 4 + wave) * 2 + t) * MT + mt) * 64 + lane) * 16);
+    };
+    auto wg_of_unit = [&](int64_t u) { return (int)(((u + 1) * p.grid - 1) / U); };
+    auto first_unit_of = [&](int wg) { return (int64_t)wg * U / p.grid; };
 
-    // ---- K slices meet in the workspace ------------------------------------------------------
-    const int nsplit = min(p.splits, (kblocks + p.kb_per_split - 1) / p.kb_per_split);
-    if (nsplit > 1) {
+    // a strip's units that this workgroup computed are done: write C, or meet the other pieces
+    auto finish_strip = [&](int strip) {
+        const int wf = wg_of_unit((int64_t)strip * p.ks);
+        const int wl = wg_of_unit((int64_t)(strip + 1) * p.ks - 1);
+        if (wf == wl) {  // the whole strip is ours
+            store_c(strip);
+            return;
+        }
         __shared__ uint32_t last_flag;
-        float* strip_ws = p.ws + (size_t)strip * p.splits * NR * 64;
-        float* slot = strip_ws + (size_t)split * NR * 64;
+        const int seg = (strip == first_strip) ? 0 : 1;
 #pragma unroll
-        for (int t = 0; t < PER_WAVE; ++t) slot[(wave * PER_WAVE + t) * 64 + lane] = part[t];
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) {
-            const uint32_t prev = atomicAdd(&p.counters[strip], 1u);
-            last_flag = (prev == (uint32_t)(nsplit - 1)) ? 1u : 0u;
-        }
-        __syncthreads();
-        if (!last_flag) return;
-        __threadfence();
-        if (tid == 0) p.counters[strip] = 0u;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < PER_WAVE; ++t) {
-            const int ri = wave * PER_WAVE + t;
-            float s = 0.f;
-            for (int q = 0; q < nsplit; ++q)
-                s += (q == split) ? part[t] : strip_ws[((size_t)q * NR + ri) * 64 + lane];
-            part[t] = s;
+            for (int mt = 0; mt < MT; ++mt) buf_store16_dev(ws, slot_off(w, seg, t, mt), f4_bits(acc[t][mt]));
+        wait_vmcnt<0>();  // the partial is stored (this also drains the ring's loads in flight)
+        lds_barrier();
+        if (tid == 0)
+            last_flag = (counter_arrive(&p.counters[strip]) == (uint32_t)(wl - wf)) ? 1u : 0u;
+        lds_barrier();
+        if (last_flag) {
+            if (tid == 0) counter_reset(&p.counters[strip]);
+            // pieces in K order are the workgroups wf .. wl; all loads of a batch are issued
+            // before any add, and the adds run in piece order
+            constexpr int PB = 16 / MT;
+            f32x4 sum[2][MT];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) sum[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int b0 = wf; b0 <= wl; b0 += PB) {
+                f32x4 v[PB][2][MT];
+#pragma unroll
+                for (int q = 0; q < PB; ++q) {
+                    const int wg = b0 + q;
+                    const int sq = (wg <= wl && first_unit_of(wg) / p.ks == strip) ? 0 : 1;
+                    const bool load = wg <= wl && wg != w;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            v[q][t][mt] = bits_f4(buf_load16_dev(ws, sel_off(load, slot_off(wg, sq, t, mt))));
+                }
+#pragma unroll
+                for (int q = 0; q < PB; ++q) {
+                    const int wg = b0 + q;
+                    if (wg > wl) break;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) sum[t][mt] += (wg == w) ? acc[t][mt] : v[q][t][mt];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[t][mt] = sum[t][mt];
+            store_c(strip);
         }
-    }
+    };
 
-    // ---- bf16 store ----------------------------------------------------------------------------
-    // register index ri = (c * MT + mt) * 4 + r holds row m = 16 mt + (lane & 15) and strip
-    // column 8 * (4 * (lane >> 4) + r) + c.
+    // ---- the ring: STAGES - 1 units in flight while one is consumed --------------------------
 #pragma unroll
-    for (int t = 0; t < PER_WAVE; ++t) {
-        const int ri = wave * PER_WAVE + t;
-        const int r = ri & 3, mt = (ri >> 2) % MT, c = (ri >> 2) / MT;
-        const int m = 16 * mt + c16;
-        const int n = n0 + 8 * (4 * g + r) + c;
-        if (m < p.M && n < p.N) {
-            const __bf16 h = (__bf16)part[t];
-            p.C[(size_t)m * p.ldc + n] = __builtin_bit_cast(uint16_t, h);
+    for (int i = 0; i < STAGES - 1; ++i) issue_unit(i);
+    for (int i = 0; i < nunits; ++i) {
+        wait_vmcnt<T::LOADS * (STAGES - 2)>();  // this wave's loads for unit i have landed
+        lds_barrier();    // ... and every wave's; every wave is also done reading unit i - 1
+        issue_unit(i + STAGES - 1);             // refills the slot unit i - 1 used
+        compute_unit(i);
+        const int64_t u = u_begin + i;
+        if (i == nunits - 1 || (u + 1) % p.ks == 0) {  // last unit of a strip in this range
+            finish_strip((int)(u / p.ks));
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{};
         }
     }
+    wait_vmcnt<0>();
 }
 
 hipError_t configure_skinny_kernels() {
-    // the wave sum uses up to 128 KB of dynamic LDS (4 waves x 32 floats x 4 tiles x 64 lanes)
-    const int max_lds = 4 * 32 * 4 * 64 * (int)sizeof(float);
     hipError_t e = hipSuccess;
-    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<1>::LDS_BYTES);
+    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<2>::LDS_BYTES);
+    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<3>::LDS_BYTES);
+    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<4>::LDS_BYTES);
     return e;
 }
 
-hipError_t launch_skinny_gemm(int mtiles, const SkinnyArgs& a, hipStream_t s) {
-    const int grid = a.strips * a.splits;
-    const size_t lds = (size_t)4 * 32 * mtiles * 64 * sizeof(float);
+int skinny_slot_floats(int mtiles) {
     switch (mtiles) {
-        case 1: skinny_gemm_kernel<1><<<grid, 256, lds, s>>>(a); break;
-        case 2: skinny_gemm_kernel<2><<<grid, 256, lds, s>>>(a); break;
-        case 3: skinny_gemm_kernel<3><<<grid, 256, lds, s>>>(a); break;
-        case 4: skinny_gemm_kernel<4><<<grid, 256, lds, s>>>(a); break;
+        case 1: return SkinnyTraits<1>::SLOT_FLOATS;
+        case 2: return SkinnyTraits<2>::SLOT_FLOATS;
+        case 3: return SkinnyTraits<3>::SLOT_FLOATS;
+        default: return SkinnyTraits<4>::SLOT_FLOATS;
+    }
+}
+
+hipError_t launch_skinny_gemm(int mtiles, const SkinnyArgs& a, hipStream_t s) {
+    const int grid = a.grid;
+    switch (mtiles) {
+        case 1: skinny_gemm_kernel<1><<<grid, 256, SkinnyTraits<1>::LDS_BYTES, s>>>(a); break;
+        case 2: skinny_gemm_kernel<2><<<grid, 256, SkinnyTraits<2>::LDS_BYTES, s>>>(a); break;
+        case 3: skinny_gemm_kernel<3><<<grid, 256, SkinnyTraits<3>::LDS_BYTES, s>>>(a); break;
+        case 4: skinny_gemm_kernel<4><<<grid, 256, SkinnyTraits<4>::LDS_BYTES, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

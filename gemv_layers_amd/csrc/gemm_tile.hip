@@ -59,7 +59,7 @@ tile_gemm_kernel(TileArgs p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
     // ---- which tile and K range ------------------------------------------------------------
@@ -207,30 +207,27 @@ tile_gemm_kernel(TileArgs p) {
         const int npieces = min(p.splits, (kt_total + p.kt_per_split - 1) / p.kt_per_split);
         if (npieces > 1) {
             __shared__ uint32_t last_flag;
-            float* slot_base = p.ws + (size_t)tile * p.splits * (BM * BN);
-            float* mine = slot_base + (size_t)piece * (BM * BN);
-            // fragment-order layout: [wave][ni][mi][r/4][lane][4]
+            // slot layout (floats, fragment order): [wave][ni][mi][r/4][lane][4]
+            const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.ws + (size_t)tile * p.splits * (BM * BN));
+            const uint32_t slot_bytes = (uint32_t)(BM * BN) * 4u;
 #pragma unroll
             for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
                 for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const size_t off = ((((size_t)wave * TN + ni) * TM + mi) * 4 + q) * 256 + lane * 4;
+                        const uint32_t off = (uint32_t)(((((wave * TN + ni) * TM + mi) * 4 + q) * 256 + lane * 4) * 4);
                         f32x4 v = {acc[ni][mi][4 * q], acc[ni][mi][4 * q + 1], acc[ni][mi][4 * q + 2],
                                    acc[ni][mi][4 * q + 3]};
-                        *reinterpret_cast<f32x4*>(mine + off) = v;
+                        buf_store16_dev(ws, (uint32_t)piece * slot_bytes + off, f4_bits(v));
                     }
-            __threadfence();
+            wait_all_memory();
             __syncthreads();
-            if (tid == 0) {
-                const uint32_t prev = atomicAdd(&p.counters[tile], 1u);
-                last_flag = (prev == (uint32_t)(npieces - 1)) ? 1u : 0u;
-            }
+            if (tid == 0)
+                last_flag = (counter_arrive(&p.counters[tile]) == (uint32_t)(npieces - 1)) ? 1u : 0u;
             __syncthreads();
             if (!last_flag) return;
-            __threadfence();
-            if (tid == 0) p.counters[tile] = 0u;
+            if (tid == 0) counter_reset(&p.counters[tile]);
             // sum the pieces in K order: piece 0 first
 #pragma unroll
             for (int ni = 0; ni < TN; ++ni)
@@ -238,7 +235,7 @@ tile_gemm_kernel(TileArgs p) {
                 for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const size_t off = ((((size_t)wave * TN + ni) * TM + mi) * 4 + q) * 256 + lane * 4;
+                        const uint32_t off = (uint32_t)(((((wave * TN + ni) * TM + mi) * 4 + q) * 256 + lane * 4) * 4);
                         f32x4 s = {0.f, 0.f, 0.f, 0.f};
                         for (int pc = 0; pc < npieces; ++pc) {
                             f32x4 v;
@@ -246,7 +243,7 @@ tile_gemm_kernel(TileArgs p) {
                                 v = f32x4{acc[ni][mi][4 * q], acc[ni][mi][4 * q + 1], acc[ni][mi][4 * q + 2],
                                           acc[ni][mi][4 * q + 3]};
                             else
-                                v = *reinterpret_cast<const f32x4*>(slot_base + (size_t)pc * (BM * BN) + off);
+                                v = bits_f4(buf_load16_dev(ws, (uint32_t)pc * slot_bytes + off));
                             s += v;
                         }
                         acc[ni][mi][4 * q] = s[0];

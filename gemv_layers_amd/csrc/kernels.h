@@ -55,16 +55,18 @@ struct SkinnyArgs {
     uint16_t* C;
     int M, N, K;
     int lda, ldb, ldc;
-    int strips;          // column strips of B (width kSkinnyStrip columns)
-    int splits;          // K slices per strip
-    int kb_per_split;    // 32-row k-blocks per slice
-    float* ws;           // splits * strips * 64 * kSkinnyStrip floats
+    int strips;          // column strips of B (kSkinnyStrip columns each)
+    int ks;              // 64-row stages per strip, ceil(K / 64)
+    int grid;            // workgroups; workgroup w takes units [w U / grid, (w+1) U / grid) of the
+                         // strip-major list of U = strips * ks (strip, stage) units
+    float* ws;           // 2 * grid * skinny_slot_floats(mtiles) floats
     uint32_t* counters;  // one per strip, zero between launches
 };
 constexpr int kSkinnyStrip = 128;   // columns per workgroup
-constexpr int kSkinnyKBlock = 32;   // k rows per wave step
+constexpr int kSkinnyStage = 64;    // k rows per streamed unit
 hipError_t launch_skinny_gemm(int mtiles, const SkinnyArgs& a, hipStream_t s);
 hipError_t configure_skinny_kernels();
+int skinny_slot_floats(int mtiles);  // workspace floats per (strip, K slice)
 
 // ---- misc ------------------------------------------------------------------------------------
 hipError_t launch_zero_c(uint16_t* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);

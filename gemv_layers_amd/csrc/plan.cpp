@@ -52,24 +52,21 @@ static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) 
     p.mtiles = (int)cdiv(M, 16);
     p.threads = 256;
     p.strips = (int)cdiv(N, kSkinnyStrip);
-    const int64_t kblocks = cdiv(K, kSkinnyKBlock);
-    const int per_cu = p.mtiles <= 2 ? 2 : 1;  // LDS for the wave sum is 32 KB per 16-row tile
-    const int64_t target = (int64_t)dev.cus * per_cu;
-    int64_t s = std::max<int64_t>(1, (target + p.strips / 2) / p.strips);
-    s = std::min<int64_t>(s, kblocks);
-    const int64_t slot_floats = (int64_t)32 * p.mtiles * 64;
-    while (s > 1 && (int64_t)p.strips * s * slot_floats > dev.ws_floats) --s;
-    if (s > 1 && p.strips > dev.ws_counters) s = 1;
-    p.kb_per_split = (int)cdiv(kblocks, s);
-    p.splits = (int)cdiv(kblocks, p.kb_per_split);
-    p.grid = (int64_t)p.strips * p.splits;
-    p.slots = (int64_t)dev.cus * per_cu;
-    if (p.splits > 1) {
-        p.ws_floats = (int64_t)p.strips * p.splits * slot_floats;
-        p.counters = p.strips;
-    }
+    p.ks = (int)cdiv(K, kSkinnyStage);
+    const int64_t units = (int64_t)p.strips * p.ks;
+    // one workgroup per CU (the LDS ring takes ~128 KB), each with a balanced range of units
+    p.slots = dev.cus;
+    p.grid = std::min<int64_t>(units, dev.cus);
+    const int64_t slot_floats = skinny_slot_floats(p.mtiles);
+    // two partial slots per workgroup; fall back to one unit range per strip (no partials) if
+    // the workspace or the counters cannot hold them
+    if (2 * p.grid * slot_floats > dev.ws_floats || p.strips > dev.ws_counters) p.grid = p.strips;
+    p.ws_floats = 2 * p.grid * slot_floats;
+    p.counters = p.strips;
+    p.splits = (int)cdiv(p.grid, p.strips);  // pieces per strip, about
     finish_waves(p);
-    p.reason = "M <= 64: weights streamed once, " + std::to_string(p.splits) + " K slice(s)";
+    p.reason = "M <= 64: weights streamed once, " + std::to_string(p.grid) +
+               " workgroups over " + std::to_string(units) + " strip stages";
     return p;
 }
 
@@ -97,12 +94,16 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
         set_tile(p, kTile128x128w4, M, N);
         p.reason = "256x256 grid below one wave: 128x128 tiles";
     }
+    if (dev.force_tile_cfg >= 0 && dev.force_tile_cfg < kTileConfigCount) {
+        set_tile(p, dev.force_tile_cfg, M, N);
+        p.reason = "tile configuration forced";
+    }
     p.group_m = (int)std::min<int64_t>(4, p.tiles_m);
     p.sched = kSchedDataParallel;
     p.splits = 1;
     p.kt_per_split = (int)kt_total;
     // 128x128 tiles: LDS 64 KB per workgroup, so two fit on a CU
-    const int per_cu = (p.tile_cfg == kTile128x128w4) ? 2 : 1;
+    const int per_cu = (p.tile_cfg == kTile128x128w4 || p.tile_cfg == kTile256x256w8) ? 2 : 1;
     p.slots = (int64_t)dev.cus * per_cu;
     if (p.tiles < p.slots && kt_total > 1) {
         // split K over the idle slots; pieces are summed in K order by the last arriver
@@ -169,14 +170,14 @@ std::string plan_json(const Plan& p, int64_t M, int64_t N, int64_t K) {
              "{\"M\": %lld, \"N\": %lld, \"K\": %lld, \"kernel\": \"%s\", \"bm\": %d, \"bn\": %d, "
              "\"bk\": %d, \"threads\": %d, \"tiles_m\": %lld, \"tiles_n\": %lld, \"tiles\": %lld, "
              "\"schedule\": \"%s\", \"splits\": %d, \"kt_per_split\": %d, \"group_m\": %d, "
-             "\"nxcd\": %d, \"mtiles\": %d, \"strips\": %d, \"kb_per_split\": %d, \"grid\": %lld, "
+             "\"nxcd\": %d, \"mtiles\": %d, \"strips\": %d, \"ks\": %d, \"grid\": %lld, "
              "\"slots\": %lld, \"waves\": %lld, \"wave_eff\": %.6f, \"ws_floats\": %lld, "
              "\"reason\": \"%s\"}",
              (long long)M, (long long)N, (long long)K, kernel_name(p.kernel), p.bm, p.bn, p.bk,
              p.threads, (long long)p.tiles_m, (long long)p.tiles_n, (long long)p.tiles,
              p.kernel == kKernTile ? (p.sched == kSchedSplitK ? "split-k" : "data-parallel")
                                    : (p.kernel == kKernSkinny ? "strips" : "-"),
-             p.splits, p.kt_per_split, p.group_m, p.nxcd, p.mtiles, p.strips, p.kb_per_split,
+             p.splits, p.kt_per_split, p.group_m, p.nxcd, p.mtiles, p.strips, p.ks,
              (long long)p.grid, (long long)p.slots, (long long)p.waves, p.wave_eff,
              (long long)p.ws_floats, p.reason.c_str());
     return std::string(buf);

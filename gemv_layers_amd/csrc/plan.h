@@ -25,7 +25,7 @@ struct Plan {
     // skinny kernel
     int mtiles = 0;          // 16-row tiles of M
     int strips = 0;          // 128-column strips
-    int kb_per_split = 0;    // 32-row k-blocks per slice
+    int ks = 0;              // 64-row stages per strip (skinny: units = strips * ks)
     // launch
     int64_t grid = 0;
     int64_t slots = 0;       // workgroups resident at once
@@ -41,6 +41,7 @@ struct DeviceInfo {
     int nxcd = 8;
     int64_t ws_floats = 0;   // workspace capacity
     int64_t ws_counters = 0;
+    int force_tile_cfg = -1; // debug: force a large-tile configuration (GEMM_BF16_FORCE_TILE)
 };
 
 // Wave quantization ("Kernel development on sm_120", section 4, budget 4):

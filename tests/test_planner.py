@@ -71,11 +71,14 @@ def test_decode_shapes_stream_weights(name):
     assert p["kernel"] == "skinny"
     assert p["mtiles"] == _cdiv(w.M, 16)
     assert p["strips"] == _cdiv(w.N, 128)
-    kblocks = _cdiv(w.K, 32)
-    assert p["splits"] * p["kb_per_split"] >= kblocks
-    assert (p["splits"] - 1) * p["kb_per_split"] < kblocks
-    assert p["grid"] == p["strips"] * p["splits"]
-    assert p["grid"] >= 256  # enough workgroups to cover every CU
+    assert p["ks"] == _cdiv(w.K, 64)
+    # one workgroup per CU, each with a balanced range of (strip, stage) units
+    assert p["grid"] == 256 and p["waves"] == 1 and p["wave_eff"] == 1.0
+
+
+def test_skinny_small_problem_has_one_unit_per_workgroup():
+    p = g.gemm_plan_describe(3, 256, 128, 256)
+    assert p["kernel"] == "skinny" and p["grid"] == 2 * 2
 
 
 def test_dispatch_threshold_and_degenerate():
