@@ -167,6 +167,7 @@ int gemm_init(int device) {
     if (rc == GEMM_OK && hipMemset(ds.counters, 0, kWsCounters * sizeof(uint32_t)) != hipSuccess)
         rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_skinny_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
+    if (rc == GEMM_OK && glk::configure_tile_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && hipDeviceSynchronize() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK) {
         ds.ready = true;

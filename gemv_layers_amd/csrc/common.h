@@ -119,12 +119,17 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
 // later LDS read as possibly depending on it (it would wait for all loads in flight before each
 // read); callers order it explicitly with wait_vmcnt<>() and a barrier. Offsets at or beyond the
 // descriptor's range deliver zeros.
+// (m0 is reserved, so clang warns that listing it as clobbered does not make it save m0; nothing
+// in these kernels keeps a value in m0 across the statement.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_base, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(lds_base), "v"(voff), "s"(rsrc)
                  : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // float32 pair -> two bf16 (round to nearest even; gfx950 v_cvt_pk_bf16_f32), low half = lo.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -1,26 +1,28 @@
 // Large-tile bf16 GEMM for gfx950: C = A * B, float32 accumulation on MFMA, bf16 output.
 //
-// Design (spark-kernels post, "the bf16 gemm": tiles staged HBM -> shared memory, more than one
-// stage in flight, an XOR-swizzled shared tile instead of padding, the epilogue written from the
-// accumulator registers; "stream-k proper": grouped tile order for cache reuse and a split-tile
-// fixup summed in K order so every run gives the same bits):
+// Design (spark-kernels post, "the bf16 gemm": tiles staged HBM -> shared memory with several
+// stages in flight, an XOR-swizzled shared tile instead of padding, the epilogue written from the
+// accumulator registers; "the copies were the problem": take the copies out of the compute
+// waves' instruction stream and avoid a full barrier's cost per k step; "stream-k proper":
+// grouped tile order for cache reuse and a split-tile fixup summed in K order so every run gives
+// the same bits):
 //
 // * One workgroup per (tile, K piece). Workgroup ids are first remapped so that each XCD's
 //   round-robin share of the grid is a contiguous run of tiles, then walked in grouped order
 //   (group_m tile rows at a time), so the tiles resident on one XCD share A rows and B columns
 //   in that XCD's L2.
-// * K advances in steps of 64. Each step's A tile (BM x 64) and B tile (64 x BN) are fetched
-//   with 16-byte buffer loads into registers one step ahead of use, then written to one of two
-//   LDS stages. Out-of-range rows, columns and k are fetched as zeros by pointing their offset
-//   past the descriptor's range, so ragged edges need no branches.
-// * Both operands sit in LDS K-contiguous ([row][k] for A, [col][k] for B), 128 bytes per row
-//   split into eight 16-byte chunks stored at chunk ^ (row & 7). B arrives N-contiguous, so each
-//   thread fetches an 8 x 8 block of B and transposes it in registers (v_perm) before its LDS
-//   write; the MFMA operand of B then becomes one 16-byte LDS read per lane, like A's.
+// * K advances in steps of BK = 32 through an LDS ring of STAGES = 4 stages. A stage's A tile
+//   (BM x 32) and B tile (32 x BN) are copied HBM -> LDS by direct-to-LDS buffer loads (1 KB per
+//   wave instruction, no registers), STAGES - 1 steps ahead of use; one barrier per step, with no
+//   memory fence, so the later stages' loads stay in flight.
+// * A sits in LDS K-contiguous (64-byte rows, 16-byte chunks stored at chunk ^ ((row >> 1) & 3))
+//   and is read with ds_read_b128. B stays row-major (N-contiguous, 32-byte column groups stored
+//   at group ^ (k & 7)); its MFMA operand, 8 consecutive k for one column, comes from
+//   ds_read_b64_tr_b16, which transposes 4 x 16 blocks on the way out of LDS.
 // * v_mfma_f32_32x32x16_bf16 with B as the first operand and A as the second, so each lane's
 //   accumulator holds 4 consecutive columns of one row of C: the epilogue converts pairs with
 //   v_cvt_pk_bf16_f32 (round to nearest even) and stores 8 bytes per lane.
-// * Split pieces store float32 partials to a workspace slot, publish with a release fence and
+// * Split pieces store float32 partials to a workspace slot with device-scope stores, then bump
 //   an arrival counter; the last arriver adds all pieces of the tile in K order, writes bf16 and
 //   returns the counter to zero for the next launch (no memset, no spin-waiting).
 
@@ -29,33 +31,50 @@
 
 namespace glk {
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 template <int BM, int BN, int WM, int WN>
 struct TileTraits {
-    static constexpr int BK = 64;
-    static constexpr int NT = WM * WN * 64;
+    static constexpr int BK = 32;
+    static constexpr int STAGES = 4;
+    static constexpr int NW = WM * WN;
+    static constexpr int NT = NW * 64;
     static constexpr int WTM = BM / WM;
     static constexpr int WTN = BN / WN;
     static constexpr int TM = WTM / 32;
     static constexpr int TN = WTN / 32;
-    static constexpr int A_CH = BM * BK / 8 / NT;          // 16-byte A chunks per thread
-    static constexpr int B_BLOCKS = (BK / 8) * (BN / 8);   // 8x8 B blocks per stage
-    static constexpr int B_BL = B_BLOCKS >= NT ? B_BLOCKS / NT : 1;  // per active thread
-    static constexpr bool B_ALL = B_BLOCKS >= NT;          // every thread stages B
-    static constexpr int STAGE = (BM + BN) * BK;           // bf16 elements per LDS stage
-    static_assert(A_CH >= 1 && A_CH * NT * 8 == BM * BK, "A staging must divide evenly");
-    static_assert(B_ALL ? (B_BL * NT == B_BLOCKS) : (NT % B_BLOCKS == 0), "B staging must divide evenly");
+    static constexpr int A_BYTES = BM * BK * 2;             // 64-byte rows
+    static constexpr int B_BYTES = BK * BN * 2;             // 2*BN-byte rows
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int A_INSTR = A_BYTES / 1024;          // 1 KB direct-to-LDS instructions
+    static constexpr int B_INSTR = B_BYTES / 1024;
+    static constexpr int A_PER_WAVE = A_INSTR / NW;
+    static constexpr int B_PER_WAVE = B_INSTR / NW;
+    static constexpr int LOADS = A_PER_WAVE + B_PER_WAVE;   // per wave per stage
+    static constexpr int B_CHUNKS = BN / 8;                 // 16-byte chunks per B row
+    static constexpr int B_ROWS_PER_INSTR = 1024 / (2 * BN);
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static_assert(A_PER_WAVE * NW == A_INSTR && B_PER_WAVE * NW == B_INSTR, "loads split evenly");
+    static_assert(BN >= 128, "B swizzle needs at least 8 column groups per row");
     static_assert(TM >= 1 && TN >= 1, "wave tile must hold whole 32x32 MFMA tiles");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
 };
+
+// A: physical 16-byte chunk of logical chunk c (0..3) in row m
+__device__ __forceinline__ int a_swz(int c, int m) { return c ^ ((m >> 1) & 3); }
+// B: physical 32-byte column group of logical group u in k row k
+__device__ __forceinline__ int b_swz(int u, int k) { return u ^ (k & 7); }
 
 template <int BM, int BN, int WM, int WN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
                                amdgpu_waves_per_eu(1, 1)))
 tile_gemm_kernel(TileArgs p) {
     using T = TileTraits<BM, BN, WM, WN>;
-    constexpr int BK = T::BK, NT = T::NT, TM = T::TM, TN = T::TN;
-    constexpr int A_CH = T::A_CH, B_BL = T::B_BL;
-    constexpr bool B_ALL = T::B_ALL;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::STAGE];
+    constexpr int BK = T::BK, STAGES = T::STAGES, TM = T::TM, TN = T::TN;
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -85,73 +104,47 @@ tile_gemm_kernel(TileArgs p) {
         kt_begin = piece * p.kt_per_split;
         kt_end = min(kt_total, kt_begin + p.kt_per_split);
     }
+    const int nsteps = max(kt_end - kt_begin, 0);
 
-    // ---- per-thread load coordinates ---------------------------------------------------------
-    // A: chunk i covers row a_m[i] of the tile, k-chunk a_kc (same for all i).
-    const int a_kc = tid & 7;
-    uint32_t a_off[A_CH];
-    bool a_row_ok[A_CH];
+    // ---- direct-to-LDS load addressing ---------------------------------------------------------
+    // A instruction i of this wave: tile rows 16 (wave * A_PER_WAVE + i) .. +15; lane l lands at
+    // byte 16 l = row + l/4, physical chunk l%4, and fetches the logical chunk stored there.
+    uint32_t a_off[T::A_PER_WAVE];
+    int a_kchunk[T::A_PER_WAVE];
+    bool a_row_ok[T::A_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        const int m = i * (NT / 8) + (tid >> 3);
-        a_off[i] = (uint32_t)(m * p.lda + a_kc * 8) * 2u;
-        a_row_ok[i] = (m0 + m) < p.M;
+    for (int i = 0; i < T::A_PER_WAVE; ++i) {
+        const int row = 16 * (wave * T::A_PER_WAVE + i) + (lane >> 2);
+        a_kchunk[i] = a_swz(lane & 3, row);  // the swizzle is an involution
+        a_row_ok[i] = m0 + row < p.M;
+        a_off[i] = (uint32_t)(row * p.lda + 8 * a_kchunk[i]) * 2u;
     }
-    // B: block j covers k rows 8*b_kb .. +7 and columns 8*b_nb[j] .. +7 of the tile.
-    const int b_kb = tid & 7;
-    uint32_t b_off[B_BL];
-    bool b_col_ok[B_BL];
+    // B instruction i: k rows R0 .. R0 + B_ROWS_PER_INSTR - 1; lane l -> row R0 + l / B_CHUNKS,
+    // physical chunk l % B_CHUNKS (group pc/2, half pc%2), holding logical group b_swz(pc/2, k).
+    uint32_t b_off[T::B_PER_WAVE];
 #pragma unroll
-    for (int j = 0; j < B_BL; ++j) {
-        const int nb = j * (NT / 8) + (tid >> 3);
-        b_off[j] = (uint32_t)(8 * b_kb * p.ldb + 8 * nb) * 2u;
-        b_col_ok[j] = (n0 + 8 * nb) < p.N;
+    for (int i = 0; i < T::B_PER_WAVE; ++i) {
+        const int k = (wave * T::B_PER_WAVE + i) * T::B_ROWS_PER_INSTR + lane / T::B_CHUNKS;
+        const int pc = lane % T::B_CHUNKS;
+        const int col = 16 * b_swz(pc >> 1, k) + 8 * (pc & 1);
+        b_off[i] = sel_off(n0 + col < p.N, (uint32_t)(k * p.ldb + col) * 2u);
     }
-    const uint32_t ldb_bytes = (uint32_t)p.ldb * 2u;
-    const bool b_active = B_ALL || tid < T::B_BLOCKS;  // threads that stage B
 
-    u32x4 ra[A_CH];
-    u32x4 rb[B_BL][8];
-
-    auto load_stage = [&](int kt) {
-        const int k0 = kt * BK;
-        const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(p.A + (size_t)m0 * p.lda + k0);
-        const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(p.B + (size_t)k0 * p.ldb + n0);
-        const bool a_k_ok = (k0 + a_kc * 8) < p.K;
+    auto issue_step = [&](int i) {  // i-th k step of this workgroup, into ring slot i % STAGES
+        char* st = lds + (i % STAGES) * T::STAGE_BYTES;
+        const uint32_t st_lds = lds_addr(st);
+        const int k0 = (kt_begin + i) * BK;
+        const int krows = (i < nsteps) ? min(BK, p.K - k0) : 0;  // uniform
+        const i32x4 ar = rsrc_words(p.A + (size_t)m0 * p.lda + k0, kBufRecords);
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i)
-            ra[i] = buf_load16(ra_rsrc, (a_row_ok[i] && a_k_ok) ? a_off[i] : kBufInvalid);
-        if (!b_active) return;
-#pragma unroll
-        for (int j = 0; j < B_BL; ++j) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const bool ok = b_col_ok[j] && (k0 + 8 * b_kb + r) < p.K;
-                rb[j][r] = buf_load16(rb_rsrc, ok ? b_off[j] + (uint32_t)r * ldb_bytes : kBufInvalid);
-            }
+        for (int t = 0; t < T::A_PER_WAVE; ++t) {
+            const bool ok = a_row_ok[t] && 8 * a_kchunk[t] < krows;
+            dma16(ar, st_lds + (wave * T::A_PER_WAVE + t) * 1024, sel_off(ok, a_off[t]));
         }
-    };
-
-    auto store_stage = [&](int stage) {
-        uint16_t* sa = lds + stage * T::STAGE;
-        uint16_t* sb = sa + BM * BK;
+        const i32x4 br = rsrc_words(p.B + (size_t)k0 * p.ldb + n0, (uint32_t)krows * (uint32_t)p.ldb * 2u);
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int m = i * (NT / 8) + (tid >> 3);
-            *reinterpret_cast<u32x4*>(sa + m * BK + ((a_kc ^ (m & 7)) * 8)) = ra[i];
-        }
-        if (!b_active) return;
-#pragma unroll
-        for (int j = 0; j < B_BL; ++j) {
-            const int nb = j * (NT / 8) + (tid >> 3);
-            u32x4 tcol[8];
-            transpose8x8_b16(rb[j], tcol);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int n = 8 * nb + c;
-                *reinterpret_cast<u32x4*>(sb + n * BK + ((b_kb ^ c) * 8)) = tcol[c];
-            }
-        }
+        for (int t = 0; t < T::B_PER_WAVE; ++t)
+            dma16(br, st_lds + T::A_BYTES + (wave * T::B_PER_WAVE + t) * 1024, b_off[t]);
     };
 
     f32x16 acc[TN][TM];
@@ -160,45 +153,57 @@ tile_gemm_kernel(TileArgs p) {
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi) acc[ni][mi] = f32x16{};
 
-    // fragment read coordinates: lane reads row (lane & 31) of a 32-row block, k-chunk
-    // 2*kk + (lane >> 5); the swizzle term is (row & 7) == (lane & 7).
-    const int fr_row = lane & 31;
-    const int fr_half = lane >> 5;
-    const int fr_sw = lane & 7;
+    // fragment addressing
+    // A (second MFMA operand, 32 m x 16 k): lane l reads row (l % 32), k chunk 2 kk + l / 32
+    const int fa_row = lane & 31, fa_half = lane >> 5;
+    // B (first operand, 32 n x 16 k): 16-lane group G covers columns 16 (G & 1) + 0..15 and k
+    // rows 8 (G >> 1) + 0..7 in two transposed reads of 4 rows; lane j of the group addresses
+    // row j / 4 of the read's 4 and columns 4 (j % 4) .. +3.
+    const int fG = lane >> 4, fj = lane & 15;
+    const int fb_k = 8 * (fG >> 1) + (fj >> 2);
+    const int fb_n = 16 * (fG & 1) + 4 * (fj & 3);
 
-    if (kt_begin < kt_end) {
-        load_stage(kt_begin);
-        store_stage(0);
-        __syncthreads();
-        for (int kt = kt_begin; kt < kt_end; ++kt) {
-            const int cur = (kt - kt_begin) & 1;
-            const bool more = (kt + 1) < kt_end;
-            if (more) load_stage(kt + 1);
-            const uint16_t* sa = lds + cur * T::STAGE;
-            const uint16_t* sb = sa + BM * BK;
+    auto compute_step = [&](int i) {
+        const char* st = lds + (i % STAGES) * T::STAGE_BYTES;
+        const char* sb = st + T::A_BYTES;
 #pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                const int kc = 2 * kk + fr_half;
-                bf16x8 af[TM], bfr[TN];
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            bf16x8 af[TM], bx[TN];
 #pragma unroll
-                for (int mi = 0; mi < TM; ++mi) {
-                    const int m = wm * T::WTM + mi * 32 + fr_row;
-                    af[mi] = *reinterpret_cast<const bf16x8*>(sa + m * BK + ((kc ^ fr_sw) * 8));
-                }
-#pragma unroll
-                for (int ni = 0; ni < TN; ++ni) {
-                    const int n = wn * T::WTN + ni * 32 + fr_row;
-                    bfr[ni] = *reinterpret_cast<const bf16x8*>(sb + n * BK + ((kc ^ fr_sw) * 8));
-                }
-#pragma unroll
-                for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-                    for (int mi = 0; mi < TM; ++mi) acc[ni][mi] = mfma32(bfr[ni], af[mi], acc[ni][mi]);
+            for (int mi = 0; mi < TM; ++mi) {
+                const int m = wm * T::WTM + mi * 32 + fa_row;
+                af[mi] = *reinterpret_cast<const bf16x8*>(st + m * 64 + 16 * a_swz(2 * kk + fa_half, m));
             }
-            if (more) store_stage(cur ^ 1);
-            __syncthreads();
+#pragma unroll
+            for (int ni = 0; ni < TN; ++ni) {
+                const int n = wn * T::WTN + ni * 32 + fb_n;
+                i16x4 v[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = 16 * kk + fb_k + 4 * h;
+                    const char* addr = sb + k * (2 * BN) + 32 * b_swz(n >> 4, k) + 2 * (n & 15);
+                    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)addr);
+                }
+                const i16x8 x = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+                bx[ni] = __builtin_bit_cast(bf16x8, x);
+            }
+#pragma unroll
+            for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < TM; ++mi) acc[ni][mi] = mfma32(bx[ni], af[mi], acc[ni][mi]);
         }
+    };
+
+    // ---- main loop: STAGES - 1 steps in flight ----------------------------------------------
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i) issue_step(i);
+    for (int i = 0; i < nsteps; ++i) {
+        wait_vmcnt<T::LOADS * (STAGES - 2)>();  // this wave's loads for step i have landed
+        lds_barrier();   // every wave's have, and every wave is done reading step i - 1's slot
+        issue_step(i + STAGES - 1);
+        compute_step(i);
     }
+    wait_vmcnt<0>();
 
     // ---- split fixup ---------------------------------------------------------------------------
     // Lane layout of acc[ni][mi][r]: row m = wm*WTM + mi*32 + (lane & 31),
@@ -258,13 +263,13 @@ tile_gemm_kernel(TileArgs p) {
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + (size_t)m0 * p.ldc + n0);
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
-        const int m = wm * T::WTM + mi * 32 + fr_row;
+        const int m = wm * T::WTM + mi * 32 + fa_row;
         const bool m_ok = (m0 + m) < p.M;
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = wn * T::WTN + ni * 32 + 8 * q + 4 * fr_half;
+                const int n = wn * T::WTN + ni * 32 + 8 * q + 4 * fa_half;
                 const bool ok = m_ok && (n0 + n) < p.N;
                 u32x2 v = {pack_bf16x2(acc[ni][mi][4 * q], acc[ni][mi][4 * q + 1]),
                            pack_bf16x2(acc[ni][mi][4 * q + 2], acc[ni][mi][4 * q + 3])};
@@ -276,29 +281,41 @@ tile_gemm_kernel(TileArgs p) {
 
 TileShape tile_shape(int cfg) {
     switch (cfg) {
-        case kTile256x256w4: return {256, 256, 64, 256};
-        case kTile256x256w8: return {256, 256, 64, 512};
-        case kTile128x128w4: return {128, 128, 64, 256};
+        case kTile256x256w4: return {256, 256, 32, 256};
+        case kTile256x256w8: return {256, 256, 32, 512};
+        case kTile128x128w4: return {128, 128, 32, 256};
         default: return {0, 0, 0, 0};
     }
 }
 
-hipError_t launch_tile_gemm(int cfg, const TileArgs& a, int grid, hipStream_t s) {
-    const TileShape t = tile_shape(cfg);
-    switch (cfg) {
-        case kTile256x256w4:
-            tile_gemm_kernel<256, 256, 2, 2><<<grid, t.threads, 0, s>>>(a);
-            break;
-        case kTile256x256w8:
-            tile_gemm_kernel<256, 256, 2, 4><<<grid, t.threads, 0, s>>>(a);
-            break;
-        case kTile128x128w4:
-            tile_gemm_kernel<128, 128, 2, 2><<<grid, t.threads, 0, s>>>(a);
-            break;
-        default:
-            return hipErrorInvalidValue;
-    }
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_cfg(const TileArgs& a, int grid, hipStream_t s) {
+    using T = TileTraits<BM, BN, WM, WN>;
+    tile_gemm_kernel<BM, BN, WM, WN><<<grid, T::NT, T::LDS_BYTES, s>>>(a);
     return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t configure_cfg() {
+    return hipFuncSetAttribute((const void*)tile_gemm_kernel<BM, BN, WM, WN>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               TileTraits<BM, BN, WM, WN>::LDS_BYTES);
+}
+
+hipError_t configure_tile_kernels() {
+    hipError_t e = configure_cfg<256, 256, 2, 2>();
+    if (e == hipSuccess) e = configure_cfg<256, 256, 2, 4>();
+    if (e == hipSuccess) e = configure_cfg<128, 128, 2, 2>();
+    return e;
+}
+
+hipError_t launch_tile_gemm(int cfg, const TileArgs& a, int grid, hipStream_t s) {
+    switch (cfg) {
+        case kTile256x256w4: return launch_cfg<256, 256, 2, 2>(a, grid, s);
+        case kTile256x256w8: return launch_cfg<256, 256, 2, 4>(a, grid, s);
+        case kTile128x128w4: return launch_cfg<128, 128, 2, 2>(a, grid, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace glk

@@ -24,7 +24,7 @@ struct TileArgs {
     int nxcd;           // XCDs the hardware deals workgroups over (8 on MI355X), 1 = no remap
     int sched;          // TileSchedule
     int splits;         // pieces per tile (split schedule)
-    int kt_per_split;   // k-steps (of 64) per piece (split schedule)
+    int kt_per_split;   // k-steps (of the tile's BK) per piece (split schedule)
     float* ws;          // split partial slots, splits * tiles * BM * BN floats
     uint32_t* counters; // one per tile, zero between launches
 };
@@ -42,6 +42,7 @@ struct TileShape {
 };
 TileShape tile_shape(int cfg);
 hipError_t launch_tile_gemm(int cfg, const TileArgs& a, int grid, hipStream_t s);
+hipError_t configure_tile_kernels();
 
 // ---- general fallback (any alignment / leading dimension) ----------------------------------
 hipError_t launch_generic_gemm(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M,

@@ -86,7 +86,6 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     Plan p;
     p.kernel = kKernTile;
     p.nxcd = dev.nxcd;
-    const int64_t kt_total = cdiv(K, 64);
     set_tile(p, kTile256x256w4, M, N);
     if (p.tiles >= dev.cus) {
         p.reason = "256x256 tiles fill at least one wave";
@@ -98,12 +97,13 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
         set_tile(p, dev.force_tile_cfg, M, N);
         p.reason = "tile configuration forced";
     }
+    const int64_t kt_total = cdiv(K, p.bk);
     p.group_m = (int)std::min<int64_t>(4, p.tiles_m);
     p.sched = kSchedDataParallel;
     p.splits = 1;
     p.kt_per_split = (int)kt_total;
-    // 128x128 tiles: LDS 64 KB per workgroup, so two fit on a CU
-    const int per_cu = (p.tile_cfg == kTile128x128w4 || p.tile_cfg == kTile256x256w8) ? 2 : 1;
+    // 256-wide tiles take 128 KB of LDS (one workgroup per CU); 128x128 tiles take 64 KB
+    const int per_cu = (p.tile_cfg == kTile128x128w4) ? 2 : 1;
     p.slots = (int64_t)dev.cus * per_cu;
     if (p.tiles < p.slots && kt_total > 1) {
         // split K over the idle slots; pieces are summed in K order by the last arriver

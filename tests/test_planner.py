@@ -60,8 +60,9 @@ def test_small_square_splits_k():
     p = g.gemm_plan_describe(512, 512, 512, 256)
     assert p["kernel"] == "tile" and (p["bm"], p["bn"]) == (128, 128)
     assert p["schedule"] == "split-k" and p["splits"] > 1
-    assert p["splits"] * p["kt_per_split"] >= 512 // 64
-    assert (p["splits"] - 1) * p["kt_per_split"] < 512 // 64  # no empty piece
+    kt = 512 // p["bk"]
+    assert p["splits"] * p["kt_per_split"] >= kt
+    assert (p["splits"] - 1) * p["kt_per_split"] < kt  # no empty piece
 
 
 @pytest.mark.parametrize("name", [n for n in WORKLOADS if n.startswith("dec_")])
