@@ -11,10 +11,13 @@
 //   round-robin share of the grid is a contiguous run of tiles, then walked in grouped order
 //   (group_m tile rows at a time), so the tiles resident on one XCD share A rows and B columns
 //   in that XCD's L2.
-// * K advances in steps of BK = 32 through an LDS ring of STAGES = 4 stages. A stage's A tile
-//   (BM x 32) and B tile (32 x BN) are copied HBM -> LDS by direct-to-LDS buffer loads (1 KB per
-//   wave instruction, no registers), STAGES - 1 steps ahead of use; one barrier per step, with no
-//   memory fence, so the later stages' loads stay in flight.
+// * K advances in steps of BK = 32 through an LDS ring of STAGES stages (all of LDS). A stage's A
+//   tile (BM x 32) and B tile (32 x BN) are copied HBM -> LDS by direct-to-LDS buffer loads (1 KB
+//   per wave instruction, no registers), STAGES - 1 steps ahead of use; one barrier per step, with
+//   no memory fence, so the later stages' loads stay in flight.
+// * MFMA operands are double-buffered in registers: while the matrix cores run step i from one
+//   register set, the LDS reads for step i + 1 fill the other, so the MFMA stream never waits on
+//   an LDS read; each barrier therefore guards the data of the step after the next.
 // * A sits in LDS K-contiguous (64-byte rows, 16-byte chunks stored at chunk ^ ((row >> 1) & 3))
 //   and is read with ds_read_b128. B stays row-major (N-contiguous, 32-byte column groups stored
 //   at group ^ (k & 7)); its MFMA operand, 8 consecutive k for one column, comes from
@@ -38,7 +41,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 template <int BM, int BN, int WM, int WN>
 struct TileTraits {
     static constexpr int BK = 32;
-    static constexpr int STAGES = 4;
+    // ring depth: all 160 KB of LDS for a one-workgroup-per-CU tile, half of it otherwise
+    static constexpr int STAGES = ((BM * BN >= 256 * 256) ? 163840 : 81920) / ((BM + BN) * BK * 2);
     static constexpr int NW = WM * WN;
     static constexpr int NT = NW * 64;
     static constexpr int WTM = BM / WM;
@@ -60,6 +64,7 @@ struct TileTraits {
     static_assert(BN >= 128, "B swizzle needs at least 8 column groups per row");
     static_assert(TM >= 1 && TN >= 1, "wave tile must hold whole 32x32 MFMA tiles");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(STAGES >= 4, "ring depth");
     static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
 };
 
@@ -163,16 +168,20 @@ tile_gemm_kernel(TileArgs p) {
     const int fb_k = 8 * (fG >> 1) + (fj >> 2);
     const int fb_n = 16 * (fG & 1) + 4 * (fj & 3);
 
-    auto compute_step = [&](int i) {
+    struct Frags {
+        bf16x8 a[BK / 16][TM];
+        bf16x8 b[BK / 16][TN];
+    };
+
+    auto read_frags = [&](int i, Frags& f) {
         const char* st = lds + (i % STAGES) * T::STAGE_BYTES;
         const char* sb = st + T::A_BYTES;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            bf16x8 af[TM], bx[TN];
 #pragma unroll
             for (int mi = 0; mi < TM; ++mi) {
                 const int m = wm * T::WTM + mi * 32 + fa_row;
-                af[mi] = *reinterpret_cast<const bf16x8*>(st + m * 64 + 16 * a_swz(2 * kk + fa_half, m));
+                f.a[kk][mi] = *reinterpret_cast<const bf16x8*>(st + m * 64 + 16 * a_swz(2 * kk + fa_half, m));
             }
 #pragma unroll
             for (int ni = 0; ni < TN; ++ni) {
@@ -185,25 +194,48 @@ tile_gemm_kernel(TileArgs p) {
                     v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)addr);
                 }
                 const i16x8 x = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
-                bx[ni] = __builtin_bit_cast(bf16x8, x);
+                f.b[kk][ni] = __builtin_bit_cast(bf16x8, x);
             }
-#pragma unroll
-            for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-                for (int mi = 0; mi < TM; ++mi) acc[ni][mi] = mfma32(bx[ni], af[mi], acc[ni][mi]);
         }
     };
 
-    // ---- main loop: STAGES - 1 steps in flight ----------------------------------------------
+    auto mfma_frags = [&](const Frags& f) {
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+            for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < TM; ++mi) acc[ni][mi] = mfma32(f.b[kk][ni], f.a[kk][mi], acc[ni][mi]);
+    };
+
+    // ---- main loop ------------------------------------------------------------------------
+    // Before step i's MFMAs: its fragments are in registers (read during step i - 1), step i + 1
+    // is in LDS and visible, steps i + 2 .. i + STAGES - 1 are in flight.
+    Frags f0, f1;
 #pragma unroll
     for (int i = 0; i < STAGES - 1; ++i) issue_step(i);
-    for (int i = 0; i < nsteps; ++i) {
-        wait_vmcnt<T::LOADS * (STAGES - 2)>();  // this wave's loads for step i have landed
-        lds_barrier();   // every wave's have, and every wave is done reading step i - 1's slot
-        issue_step(i + STAGES - 1);
-        compute_step(i);
+    wait_vmcnt<T::LOADS * (STAGES - 2)>();
+    lds_barrier();
+    read_frags(0, f0);
+    // (reading the next fragments past the last step is harmless: that slot holds zeros or
+    // stale data that no MFMA consumes)
+#define GLK_TILE_STEP(I, CUR, NEXT)                                                          \
+    do {                                                                                     \
+        wait_vmcnt<T::LOADS * (STAGES - 3)>(); /* this wave's loads for step I + 1 landed */ \
+        lds_barrier(); /* every wave's have; all are done reading slot (I - 1) % STAGES */   \
+        issue_step((I) + STAGES - 1);          /* refills that slot */                       \
+        read_frags((I) + 1, NEXT);                                                           \
+        mfma_frags(CUR);                                                                     \
+    } while (0)
+    int i = 0;
+    for (; i + 1 < nsteps; i += 2) {
+        GLK_TILE_STEP(i, f0, f1);
+        GLK_TILE_STEP(i + 1, f1, f0);
     }
+    if (i < nsteps) GLK_TILE_STEP(i, f0, f1);
+#undef GLK_TILE_STEP
     wait_vmcnt<0>();
+    lds_barrier();  // the ring is idle from here on; its first word serves the fixup below
 
     // ---- split fixup ---------------------------------------------------------------------------
     // Lane layout of acc[ni][mi][r]: row m = wm*WTM + mi*32 + (lane & 31),
@@ -211,7 +243,7 @@ tile_gemm_kernel(TileArgs p) {
     if (p.sched == kSchedSplitK && p.splits > 1) {
         const int npieces = min(p.splits, (kt_total + p.kt_per_split - 1) / p.kt_per_split);
         if (npieces > 1) {
-            __shared__ uint32_t last_flag;
+            volatile uint32_t& last_flag = *reinterpret_cast<volatile uint32_t*>(lds);
             // slot layout (floats, fragment order): [wave][ni][mi][r/4][lane][4]
             const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.ws + (size_t)tile * p.splits * (BM * BN));
             const uint32_t slot_bytes = (uint32_t)(BM * BN) * 4u;

@@ -86,7 +86,7 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     Plan p;
     p.kernel = kKernTile;
     p.nxcd = dev.nxcd;
-    set_tile(p, kTile256x256w4, M, N);
+    set_tile(p, kTile256x256w8, M, N);
     if (p.tiles >= dev.cus) {
         p.reason = "256x256 tiles fill at least one wave";
     } else {
