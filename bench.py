@@ -41,6 +41,26 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the tile kernel from the stored rocprofv3 FETCH_SIZE / WRITE_SIZE
+    passes (each scaled by the copy-kernel calibration), or None when there is no stored reading
+    for this workload or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"tile_gemm_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                kv[k.strip()] = v.strip()
+    from gemv_layers_amd.profiling import TILE_SOURCES, source_digest
+
+    if kv.get("source_sha256") != source_digest(TILE_SOURCES) or "traffic_bytes_per_launch" not in kv:
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -52,6 +72,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--large", action="store_true", help="also time sq8192, sq16384, mlp_up/down")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-torch", action="store_true", help="skip the torch.matmul comparison")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run the copy kernel 3 times over 256 MiB (known traffic) so that a "
+                         "counter pass over this command also calibrates FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -157,6 +181,17 @@ def main():
         peaks["empty_launch_us_back_to_back"] = round(e0.elapsed_time(e1), 3)  # ms/1000 = us
         out["measured_peaks"] = peaks
 
+    if args.copy_calibration:
+        log("copy calibration: 3 x 256 MiB")
+        nb = 256 << 20
+        csrc = torch.empty(nb // 4, dtype=torch.int32, device="cuda")
+        cdst = torch.empty_like(csrc)
+        g.gemm_fill_launch(P(csrc), nb, 0x3C003C00, sh)
+        for _ in range(3):
+            g.gemm_peak_copy_launch(P(csrc), P(cdst), nb, sh)
+        torch.cuda.synchronize()
+        del csrc, cdst
+
     # ---------------- the headline workload ----------------
     w = WORKLOADS[args.workload]
     log(f"workload {w.name} {w.M}x{w.N}x{w.K}")
@@ -192,7 +227,7 @@ def main():
     achieved = w.flops / (kern_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_PEAK_BF16_TFLOPS, 4),
-                "traffic": None}
+                "traffic": measured_traffic(w.name)}
     headline = {"kernel_us_mean": round(kern_ms * 1e3, 2),
                 "kernel_us_min": round(float(durs.min()) * 1e3, 2),
                 "kernel_us_median": round(float(np.median(durs)) * 1e3, 2),
@@ -203,8 +238,27 @@ def main():
         headline["frac_of_measured_mfma_peak"] = round(
             achieved / peaks["mfma_bf16_fp32_tflops_sustained"], 4)
 
+    # the same launches with the Infinity Cache flushed before each (a 1 GiB fill between the
+    # events, outside them), so that A and B come from HBM
+    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+    cold = []
+    for i in range(20):
+        g.gemm_fill_launch(P(flush), 1 << 30, i, sh)
+        e0, e1 = events(2)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    headline["kernel_us_mean_cache_flushed"] = round(float(np.mean(cold)) * 1e3, 2)
+    headline["kernel_us_min_cache_flushed"] = round(float(np.min(cold)) * 1e3, 2)
+    headline["tflops_cache_flushed"] = round(w.flops / (float(np.mean(cold)) * 1e-3) / 1e12, 1)
+
     # hipBLASLt through torch.matmul, comparison only
     try:
+        if args.no_torch:
+            raise RuntimeError("skipped (--no-torch)")
         for _ in range(5):
             torch.matmul(A, B)
         e0, e1 = events(2)

@@ -1,0 +1,139 @@
+"""Summaries of rocprofv3 CSV output for this library's kernels (plain Python, no GPU needed).
+
+    python -m gemv_layers_amd.profiling stats  <run_kernel_stats.csv> [--command CMD]
+    python -m gemv_layers_amd.profiling traffic --fetch <counter_collection.csv>
+        --write <counter_collection.csv> --kernel REGEX --copy-bytes N --workload NAME
+        [--algorithmic-bytes B] [--command CMD]
+
+`stats` prints the per-kernel table of a `--kernel-trace --stats --output-format csv` run.
+`traffic` turns two counter passes (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, both over a
+command that also runs the library's copy kernel on `--copy-bytes` bytes, e.g.
+`bench.py --copy-calibration`) into HBM bytes per launch of the kernel matching REGEX: each
+counter's mean KiB per dispatch of that kernel, times (known copy bytes / what the same counter
+read for the copy kernel). The output carries a sha256 of the kernel's sources so that a reader
+can tell whether the readings still describe the current kernel.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+TILE_SOURCES = ("gemv_layers_amd/csrc/gemm_tile.hip", "gemv_layers_amd/csrc/common.h",
+                "gemv_layers_amd/csrc/kernels.h")
+SKINNY_SOURCES = ("gemv_layers_amd/csrc/gemm_skinny.hip", "gemv_layers_amd/csrc/common.h",
+                  "gemv_layers_amd/csrc/kernels.h")
+COPY_KERNEL = r"peak_copy_kernel"
+
+
+def source_digest(paths=TILE_SOURCES) -> str:
+    """sha256 over the given sources (paths relative to the repository root)."""
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def kernel_stats(path: str) -> list[dict]:
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append({"name": r["Name"], "calls": int(r["Calls"]),
+                         "total_ns": float(r["TotalDurationNs"]), "avg_ns": float(r["AverageNs"]),
+                         "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"]),
+                         "percent": float(r["Percentage"])})
+    return rows
+
+
+def counter_per_dispatch(path: str, counter: str, kernel_regex: str) -> list[float]:
+    """Values of `counter` for every dispatch whose kernel name matches `kernel_regex`."""
+    rx = re.compile(kernel_regex)
+    out = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and rx.search(r["Kernel_Name"]):
+                out.append(float(r["Counter_Value"]))
+    return out
+
+
+def _mean(v: list[float]) -> float:
+    if not v:
+        raise SystemExit("no matching dispatches")
+    return sum(v) / len(v)
+
+
+def cmd_stats(a) -> None:
+    rows = kernel_stats(a.csv)
+    if a.command:
+        print(f"# command: {a.command}")
+    print(f"{'calls':>7} {'avg_us':>11} {'min_us':>10} {'max_us':>10} {'time%':>7}  kernel")
+    for r in rows[: a.top]:
+        name = r["name"] if len(r["name"]) <= 110 else r["name"][:107] + "..."
+        print(f"{r['calls']:7d} {r['avg_ns'] / 1e3:11.3f} {r['min_ns'] / 1e3:10.3f} "
+              f"{r['max_ns'] / 1e3:10.3f} {r['percent']:7.3f}  {name}")
+
+
+def cmd_traffic(a) -> None:
+    kib = 1024.0
+    f_copy = _mean(counter_per_dispatch(a.fetch, "FETCH_SIZE", COPY_KERNEL))
+    w_copy = _mean(counter_per_dispatch(a.write, "WRITE_SIZE", COPY_KERNEL))
+    f_k = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
+    w_k = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    fetch_scale = a.copy_bytes / (f_copy * kib)
+    write_scale = a.copy_bytes / (w_copy * kib)
+    fetch_b = _mean(f_k) * kib * fetch_scale
+    write_b = _mean(w_k) * kib * write_scale
+    srcs = SKINNY_SOURCES if a.sources == "skinny" else TILE_SOURCES
+    print(f"# HBM traffic per launch of the kernel matching /{a.kernel}/ on workload {a.workload}")
+    if a.command:
+        for ln in a.command.split(" ;; "):
+            print(f"# command: {ln}")
+    print(f"workload: {a.workload}")
+    print(f"kernel_regex: {a.kernel}")
+    print(f"sources: {' '.join(srcs)}")
+    print(f"source_sha256: {source_digest(srcs)}")
+    print(f"copy_kernel_bytes_each_way: {a.copy_bytes}")
+    print(f"copy_fetch_kib_per_dispatch: {f_copy:.3f}")
+    print(f"copy_write_kib_per_dispatch: {w_copy:.3f}")
+    print(f"fetch_scale: {fetch_scale:.6f}")
+    print(f"write_scale: {write_scale:.6f}")
+    print(f"kernel_dispatches: {len(f_k)} fetch, {len(w_k)} write")
+    print(f"kernel_fetch_kib_per_dispatch: {_mean(f_k):.3f}")
+    print(f"kernel_write_kib_per_dispatch: {_mean(w_k):.3f}")
+    print(f"fetch_bytes_per_launch: {fetch_b:.0f}")
+    print(f"write_bytes_per_launch: {write_b:.0f}")
+    print(f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}")
+    if a.algorithmic_bytes:
+        print(f"algorithmic_bytes_per_launch: {a.algorithmic_bytes}")
+        print(f"traffic_over_algorithmic: {(fetch_b + write_b) / a.algorithmic_bytes:.3f}")
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser(prog="python -m gemv_layers_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--top", type=int, default=12)
+    s.add_argument("--command", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--sources", choices=("tile", "skinny"), default="tile")
+    t.add_argument("--algorithmic-bytes", type=int, default=0)
+    t.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
