@@ -11,7 +11,9 @@
 // * The work is a strip-major list of units (one 64-row stage of one 128-column strip). Exactly one
 //   workgroup per CU takes a balanced, contiguous range of units (the Stream-K decomposition of
 //   the spark-kernels post, "stream-k proper"), so no partial last wave of workgroups exists; only
-//   the first and the last strip a range touches can be partial. The units stream through
+//   the first and the last strip a range touches can be partial. Ranges are dealt so that each
+//   XCD holds consecutive ones, so the pieces of a strip mostly run on one XCD and an XCD that
+//   starts late delays only its own strips. The units stream through
 //   an LDS ring of STAGES stages: each is fetched with direct-to-LDS buffer loads (16 bytes per
 //   lane, 1 KB per wave instruction, no registers involved), STAGES - 1 stages ahead of use, and
 //   carries the matching 64 columns of A (M rows) so every wave reads A from LDS.
@@ -26,9 +28,10 @@
 //   tile with zero rows (A rows past M are fetched as zeros); the matrix cores are otherwise idle
 //   in this memory-bound kernel, so the padding costs nothing.
 // * A strip whose units all fall in one workgroup is written straight to C. Otherwise each piece
-//   writes its float32 partial to the workgroup's slot with device-scope stores and bumps a
-//   per-strip counter; the last arriver loads every piece (all loads issued before any add), adds
-//   them in K order, writes bf16 and returns the counter to zero.
+//   writes its float32 partial to the workgroup's slot and bumps a per-strip counter; the last
+//   arriver loads every piece (all loads issued before any add), adds them in K order, writes
+//   bf16 and returns the counter to zero. Partials travel at device scope (written through to the
+//   device coherence point), whichever XCDs the pieces ran on.
 
 #include "common.h"
 #include "kernels.h"
@@ -73,7 +76,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // ---- this workgroup's units: [u_begin, u_end) of the strip-major (strip, stage) list -------
     const int64_t U = (int64_t)p.strips * p.ks;
-    const int w = (int)blockIdx.x;
+    const int w = xcd_remap((int)blockIdx.x, p.grid, p.nxcd);  // logical id: contiguous per XCD
     const int64_t u_begin = (int64_t)w * U / p.grid;
     const int64_t u_end = (int64_t)(w + 1) * U / p.grid;
     const int nunits = (int)(u_end - u_begin);
@@ -107,12 +110,18 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     const uint32_t dummy_lds = lds_addr(lds + T::DUMMY);
 
     // issue the loads of the workgroup's i-th unit into ring slot i % STAGES (units past the
-    // range read nothing: a zero-length descriptor)
+    // range read nothing: a zero-length descriptor). Units are issued in order, so the (strip,
+    // stage) position advances by one each call instead of being divided out of the index.
+    int iss_strip = first_strip;
+    int iss_stage = (int)(u_begin - (int64_t)first_strip * p.ks);
     auto issue_unit = [&](int i) {
         char* st = lds + (i % STAGES) * T::STAGE_BYTES;
-        const int64_t u = u_begin + i;
-        const int strip = (int)(u / p.ks);
-        const int k0 = (int)(u - (int64_t)strip * p.ks) * kSkRows;
+        const int strip = __builtin_amdgcn_readfirstlane(iss_strip);  // wave-uniform
+        const int k0 = __builtin_amdgcn_readfirstlane(iss_stage) * kSkRows;
+        if (++iss_stage == p.ks) {
+            iss_stage = 0;
+            ++iss_strip;
+        }
         const int n0 = strip * kSkinnyStrip;
         const int rows = (i < nunits) ? min(kSkRows, p.K - k0) : 0;  // uniform
         const i32x4 b_rsrc = rsrc_words(p.B + (size_t)k0 * p.ldb + n0, (uint32_t)rows * (uint32_t)p.ldb * 2u);
@@ -203,84 +212,126 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     auto wg_of_unit = [&](int64_t u) { return (int)(((u + 1) * p.grid - 1) / U); };
     auto first_unit_of = [&](int wg) { return (int64_t)wg * U / p.grid; };
 
-    // a strip's units that this workgroup computed are done: write C, or meet the other pieces
-    auto finish_strip = [&](int strip) {
-        const int wf = wg_of_unit((int64_t)strip * p.ks);
-        const int wl = wg_of_unit((int64_t)(strip + 1) * p.ks - 1);
-        if (wf == wl) {  // the whole strip is ours
-            store_c(strip);
-            return;
-        }
-        __shared__ uint32_t last_flag;
+    // pieces of `strip` belong to logical workgroups wf .. wl (in K order)
+    auto pieces_of = [&](int strip, int& wf, int& wl) {
+        wf = wg_of_unit((int64_t)strip * p.ks);
+        wl = wg_of_unit((int64_t)(strip + 1) * p.ks - 1);
+    };
+    auto store_partial = [&](int strip) {  // device scope; not waited for here
         const int seg = (strip == first_strip) ? 0 : 1;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) buf_store16_dev(ws, slot_off(w, seg, t, mt), f4_bits(acc[t][mt]));
-        wait_vmcnt<0>();  // the partial is stored (this also drains the ring's loads in flight)
+    };
+    // once every wave's partial stores of `strip` have completed: count this piece in; true for
+    // the piece that completes the strip
+    __shared__ uint32_t last_flag;
+    auto arrive = [&](int strip) -> bool {
+        int wf, wl;
+        pieces_of(strip, wf, wl);
         lds_barrier();
-        if (tid == 0)
-            last_flag = (counter_arrive(&p.counters[strip]) == (uint32_t)(wl - wf)) ? 1u : 0u;
+        if (tid == 0) last_flag = (counter_arrive(&p.counters[strip]) == (uint32_t)(wl - wf)) ? 1u : 0u;
         lds_barrier();
-        if (last_flag) {
-            if (tid == 0) counter_reset(&p.counters[strip]);
-            // pieces in K order are the workgroups wf .. wl; all loads of a batch are issued
-            // before any add, and the adds run in piece order
-            constexpr int PB = 16 / MT;
-            f32x4 sum[2][MT];
+        return last_flag != 0;
+    };
+    // the last arriver: every piece, added in K order (all loads of a batch issued before any
+    // add), written as bf16; the counter goes back to zero for the next launch
+    auto reduce = [&](int strip) {
+        int wf, wl;
+        pieces_of(strip, wf, wl);
+        if (tid == 0) counter_reset(&p.counters[strip]);
+        // a piece's slot: pieces after the first start their range inside the strip (slot 0);
+        // the first piece's range starts there too only if it starts at the strip's first unit
+        const int seg_first = (first_unit_of(wf) == (int64_t)strip * p.ks) ? 0 : 1;
+        constexpr int PB = 16 / MT;
+        f32x4 sum[2][MT];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) sum[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int b0 = wf; b0 <= wl; b0 += PB) {
-                f32x4 v[PB][2][MT];
+            for (int mt = 0; mt < MT; ++mt) sum[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b0 = wf; b0 <= wl; b0 += PB) {
+            f32x4 v[PB][2][MT];
 #pragma unroll
-                for (int q = 0; q < PB; ++q) {
-                    const int wg = b0 + q;
-                    const int sq = (wg <= wl && first_unit_of(wg) / p.ks == strip) ? 0 : 1;
-                    const bool load = wg <= wl && wg != w;
+            for (int q = 0; q < PB; ++q) {
+                const int wg = b0 + q;
+                const int sq = (wg == wf) ? seg_first : 0;
 #pragma unroll
-                    for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            v[q][t][mt] = bits_f4(buf_load16_dev(ws, sel_off(load, slot_off(wg, sq, t, mt))));
-                }
-#pragma unroll
-                for (int q = 0; q < PB; ++q) {
-                    const int wg = b0 + q;
-                    if (wg > wl) break;
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) sum[t][mt] += (wg == w) ? acc[t][mt] : v[q][t][mt];
-                }
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const uint32_t off = sel_off(wg <= wl, slot_off(wg, sq, t, mt));
+                        v[q][t][mt] = bits_f4(buf_load16_dev(ws, off));
+                    }
             }
+            // pieces past wl read as zeros (out-of-range offsets), so adding them changes nothing
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int q = 0; q < PB; ++q)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[t][mt] = sum[t][mt];
-            store_c(strip);
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) sum[t][mt] += v[q][t][mt];
         }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[t][mt] = sum[t][mt];
+        store_c(strip);
     };
 
     // ---- the ring: STAGES - 1 units in flight while one is consumed --------------------------
+    // A strip that ends inside the range (the first one the range touches, when it is shared)
+    // leaves its partial stored but unannounced: waiting for the store at once would also wait
+    // for every load of the ring behind it. Vector-memory operations complete in issue order, so
+    // by the time the loads of unit i + STAGES (issued after the store) have landed, the store has
+    // too, and the arrival is counted then, at no cost. Reductions wait for the range's end.
+    int pend = -1, pend_at = 0;  // stored, not yet counted
+    int fin = -1;                // stored at the range's last unit
+    int red0 = -1, red1 = -1;    // strips this workgroup completes
+    int cur_strip = first_strip;  // (strip, stage) of unit i
+    int cur_stage = iss_stage;
 #pragma unroll
     for (int i = 0; i < STAGES - 1; ++i) issue_unit(i);
     for (int i = 0; i < nunits; ++i) {
         wait_vmcnt<T::LOADS * (STAGES - 2)>();  // this wave's loads for unit i have landed
         lds_barrier();    // ... and every wave's; every wave is also done reading unit i - 1
+        if (pend >= 0 && i >= pend_at) {
+            if (arrive(pend)) red0 = pend;
+            pend = -1;
+        }
         issue_unit(i + STAGES - 1);             // refills the slot unit i - 1 used
         compute_unit(i);
-        const int64_t u = u_begin + i;
-        if (i == nunits - 1 || (u + 1) % p.ks == 0) {  // last unit of a strip in this range
-            finish_strip((int)(u / p.ks));
+        const int strip = cur_strip;
+        const bool strip_end = ++cur_stage == p.ks;
+        if (strip_end) {
+            cur_stage = 0;
+            ++cur_strip;
+        }
+        if (i == nunits - 1 || strip_end) {  // last unit of a strip in this range
+            int wf, wl;
+            pieces_of(strip, wf, wl);
+            if (wf == wl) {  // the whole strip is ours
+                store_c(strip);
+            } else {
+                store_partial(strip);
+                if (i == nunits - 1) {
+                    fin = strip;
+                } else {
+                    pend = strip;
+                    pend_at = i + STAGES;
+                }
+            }
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{};
         }
     }
-    wait_vmcnt<0>();
+    wait_vmcnt<0>();  // every load and partial store of this wave has completed
+    if (pend >= 0 && arrive(pend)) red0 = pend;
+    if (fin >= 0 && arrive(fin)) red1 = fin;
+    if (red0 >= 0) reduce(red0);
+    if (red1 >= 0) reduce(red1);
 }
 
 hipError_t configure_skinny_kernels() {

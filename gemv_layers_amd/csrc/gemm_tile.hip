@@ -18,7 +18,7 @@
 // * MFMA operands are double-buffered in registers: while the matrix cores run step i from one
 //   register set, the LDS reads for step i + 1 fill the other, so the MFMA stream never waits on
 //   an LDS read; each barrier therefore guards the data of the step after the next.
-// * A sits in LDS K-contiguous (64-byte rows, 16-byte chunks stored at chunk ^ ((row >> 1) & 3))
+// * A sits in LDS K-contiguous (64-byte rows, 16-byte chunks stored at chunk ^ ((row >> 2) & 3))
 //   and is read with ds_read_b128. B stays row-major (N-contiguous, 32-byte column groups stored
 //   at group ^ (k & 7)); its MFMA operand, 8 consecutive k for one column, comes from
 //   ds_read_b64_tr_b16, which transposes 4 x 16 blocks on the way out of LDS.
@@ -68,8 +68,10 @@ struct TileTraits {
     static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
 };
 
-// A: physical 16-byte chunk of logical chunk c (0..3) in row m
-__device__ __forceinline__ int a_swz(int c, int m) { return c ^ ((m >> 1) & 3); }
+// A: physical 16-byte chunk of logical chunk c (0..3) in row m. Sixteen consecutive rows (the
+// lanes one LDS cycle serves a ds_read_b128 for) then cover all 64 banks for any fixed c: the
+// four rows of a 256-byte bank line differ in m & 3, the four lines in (m >> 2) & 3.
+__device__ __forceinline__ int a_swz(int c, int m) { return c ^ ((m >> 2) & 3); }
 // B: physical 32-byte column group of logical group u in k row k
 __device__ __forceinline__ int b_swz(int u, int k) { return u ^ (k & 7); }
 

@@ -49,6 +49,7 @@ static void finish_waves(Plan& p) { wave_efficiency(p.grid, p.slots, &p.wave_eff
 static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     Plan p;
     p.kernel = kKernSkinny;
+    p.nxcd = dev.nxcd;
     p.mtiles = (int)cdiv(M, 16);
     p.threads = 256;
     p.strips = (int)cdiv(N, kSkinnyStrip);
