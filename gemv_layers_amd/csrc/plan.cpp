@@ -107,8 +107,12 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     const int per_cu = (p.tile_cfg == kTile128x128w4) ? 2 : 1;
     p.slots = (int64_t)dev.cus * per_cu;
     if (p.tiles < p.slots && kt_total > 1) {
-        // split K over the idle slots; pieces are summed in K order by the last arriver
-        int64_t s = std::min<int64_t>(kt_total, std::max<int64_t>(1, p.slots / p.tiles));
+        // split K over the idle slots; pieces are summed in K order by the last arriver. Each
+        // piece keeps at least kMinPieceSteps k-steps: the last arriver reads every other piece's
+        // float32 tile (BM*BN*4 bytes each), which costs more than a few k-steps of MFMA work.
+        constexpr int64_t kMinPieceSteps = 8;
+        int64_t s = std::min<int64_t>(kt_total / kMinPieceSteps, std::max<int64_t>(1, p.slots / p.tiles));
+        s = std::max<int64_t>(s, 1);
         const int64_t slot_floats = (int64_t)p.bm * p.bn;
         while (s > 1 && p.tiles * s * slot_floats > dev.ws_floats) --s;
         if (s > 1 && p.tiles > dev.ws_counters) s = 1;
