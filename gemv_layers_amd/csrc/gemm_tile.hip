@@ -315,7 +315,6 @@ tile_gemm_kernel(TileArgs p) {
 
 TileShape tile_shape(int cfg) {
     switch (cfg) {
-        case kTile256x256w4: return {256, 256, 32, 256};
         case kTile256x256w8: return {256, 256, 32, 512};
         case kTile128x128w4: return {128, 128, 32, 256};
         default: return {0, 0, 0, 0};
@@ -337,15 +336,13 @@ static hipError_t configure_cfg() {
 }
 
 hipError_t configure_tile_kernels() {
-    hipError_t e = configure_cfg<256, 256, 2, 2>();
-    if (e == hipSuccess) e = configure_cfg<256, 256, 2, 4>();
+    hipError_t e = configure_cfg<256, 256, 2, 4>();
     if (e == hipSuccess) e = configure_cfg<128, 128, 2, 2>();
     return e;
 }
 
 hipError_t launch_tile_gemm(int cfg, const TileArgs& a, int grid, hipStream_t s) {
     switch (cfg) {
-        case kTile256x256w4: return launch_cfg<256, 256, 2, 2>(a, grid, s);
         case kTile256x256w8: return launch_cfg<256, 256, 2, 4>(a, grid, s);
         case kTile128x128w4: return launch_cfg<128, 128, 2, 2>(a, grid, s);
         default: return hipErrorInvalidValue;

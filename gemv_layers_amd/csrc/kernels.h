@@ -31,9 +31,8 @@ struct TileArgs {
 
 // Tile configurations compiled into the library.
 enum TileConfig : int {
-    kTile256x256w4 = 0,  // 256 x 256 tile, 4 waves of 128 x 128
-    kTile256x256w8 = 1,  // 256 x 256 tile, 8 waves of 128 x 64
-    kTile128x128w4 = 2,  // 128 x 128 tile, 4 waves of 64 x 64
+    kTile256x256w8 = 0,  // 256 x 256 tile, 8 waves of 128 x 64
+    kTile128x128w4 = 1,  // 128 x 128 tile, 4 waves of 64 x 64
     kTileConfigCount
 };
 

@@ -105,6 +105,29 @@ def test_skinny_kernel_float_and_exact(M, N, K):
     check_exact(run("skinny", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"skinny int {M}x{N}x{K}")
 
 
+# Stream-K ranges of the skinny kernel that cross strip boundaries (strip counts that do not
+# divide the grid): short ranges, where a strip's piece is announced at the range's end, and long
+# ones, where a strip ending early in a range is announced mid-stream; ragged N and K included.
+STREAMK_SHAPES = [(3, 128 * 9 + 8, 64 * 37 + 8), (1, 128 * 7, 64 * 400), (2, 128 * 13, 64 * 170 + 24),
+                  (33, 128 * 11, 12872), (64, 128 * 9, 64 * 300)]
+
+
+@pytest.mark.parametrize("M,N,K", STREAMK_SHAPES)
+def test_skinny_stream_k_boundaries(M, N, K):
+    plan = g.gemm_plan_describe(M, N, K, 256, 1)
+    assert plan["kernel"] == "skinny"
+    U, G, ks = plan["strips"] * plan["ks"], plan["grid"], plan["ks"]
+    ranges = [(w * U // G, (w + 1) * U // G) for w in range(G)]
+    crossing = [(b, e) for b, e in ranges if b // ks != (e - 1) // ks]
+    assert crossing, "some range must span two strips"
+    A = matrix("normal", M, K, seed=5100 + M)
+    B = matrix("normal", K, N, seed=6100 + N, sigma=0.02)
+    check_float(run("skinny", A, B, M, N, K), A, B, M, N, K, f"skinny {M}x{N}x{K}")
+    Ai = matrix("int", M, K, seed=7100 + M)
+    Bi = matrix("int", K, N, seed=8100 + N)
+    check_exact(run("skinny", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"skinny int {M}x{N}x{K}")
+
+
 GENERIC_SHAPES = [(17, 15, 63), (5, 33, 1), (70, 9, 100), (1, 1, 1), (130, 67, 255)]
 
 

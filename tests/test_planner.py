@@ -45,12 +45,15 @@ def test_large_shapes_use_256_tiles(name):
     p = g.gemm_plan_describe(w.M, w.N, w.K, 256)
     assert p["kernel"] == "tile" and (p["bm"], p["bn"]) == (256, 256)
     tiles = _cdiv(w.M, 256) * _cdiv(w.N, 256)
-    assert p["tiles"] == tiles and p["grid"] == tiles
+    assert p["tiles"] == tiles and p["grid"] == tiles and p["schedule"] == "data-parallel"
     e, waves = g.gemm_wave_efficiency(tiles, 256)
     assert p["waves"] == waves and abs(p["wave_eff"] - e) < 1e-6
 
 
 def test_mlp_up_wave_quantization():
+    # 688 tiles on 256 slots fill 688 / 768 = 89.6% of three waves (the closed form)
+    e, waves = g.gemm_wave_efficiency(688, 256)
+    assert waves == 3 and abs(e - 688 / 768) < 1e-12
     p = g.gemm_plan_describe(4096, 11008, 4096, 256)
     assert p["tiles"] == 688 and p["waves"] == 3
     assert abs(p["wave_eff"] - 688 / 768) < 1e-6
@@ -63,6 +66,20 @@ def test_small_square_splits_k():
     kt = 512 // p["bk"]
     assert p["splits"] * p["kt_per_split"] >= kt
     assert (p["splits"] - 1) * p["kt_per_split"] < kt  # no empty piece
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (1000, 1000, 1000), (257, 264, 4104),
+                                   (300, 520, 328), (128, 128, 96), (200, 2000, 20000)])
+def test_split_pieces_keep_eight_k_steps(M, N, K):
+    # the last arriver reads every other piece's float32 tile, so a piece must carry at least
+    # eight k-steps of MFMA work; shapes with fewer k-steps in all are not split
+    p = g.gemm_plan_describe(M, N, K, 256)
+    kt = -(-K // p["bk"])
+    if p["schedule"] == "split-k":
+        assert p["kt_per_split"] >= 8 and p["splits"] >= 2
+        assert (p["splits"] - 1) * p["kt_per_split"] < kt <= p["splits"] * p["kt_per_split"]
+    else:
+        assert p["splits"] == 1 and (kt < 16 or p["tiles"] >= p["slots"])
 
 
 @pytest.mark.parametrize("name", [n for n in WORKLOADS if n.startswith("dec_")])
