@@ -60,6 +60,10 @@ struct TileTraits {
     static constexpr int B_CHUNKS = BN / 8;                 // 16-byte chunks per B row
     static constexpr int B_ROWS_PER_INSTR = 1024 / (2 * BN);
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    // The planner splits K only for tiles smaller than 256 x 256 (a grid of 256-wide tiles too
+    // small to fill the card falls back to smaller tiles first), so only those carry the split
+    // fixup, whose registers would otherwise crowd the main loop of the big tiles.
+    static constexpr bool SPLIT = BM * BN < 256 * 256;
     static_assert(A_PER_WAVE * NW == A_INSTR && B_PER_WAVE * NW == B_INSTR, "loads split evenly");
     static_assert(BN >= 128, "B swizzle needs at least 8 column groups per row");
     static_assert(TM >= 1 && TN >= 1, "wave tile must hold whole 32x32 MFMA tiles");
@@ -242,7 +246,7 @@ tile_gemm_kernel(TileArgs p) {
     // ---- split fixup ---------------------------------------------------------------------------
     // Lane layout of acc[ni][mi][r]: row m = wm*WTM + mi*32 + (lane & 31),
     // column n = wn*WTN + ni*32 + 8*(r >> 2) + 4*(lane >> 5) + (r & 3).
-    if (p.sched == kSchedSplitK && p.splits > 1) {
+    if (T::SPLIT && p.sched == kSchedSplitK && p.splits > 1) {
         const int npieces = min(p.splits, (kt_total + p.kt_per_split - 1) / p.kt_per_split);
         if (npieces > 1) {
             volatile uint32_t& last_flag = *reinterpret_cast<volatile uint32_t*>(lds);
@@ -324,6 +328,7 @@ TileShape tile_shape(int cfg) {
 template <int BM, int BN, int WM, int WN>
 static hipError_t launch_cfg(const TileArgs& a, int grid, hipStream_t s) {
     using T = TileTraits<BM, BN, WM, WN>;
+    if (!T::SPLIT && a.sched == kSchedSplitK && a.splits > 1) return hipErrorInvalidValue;
     tile_gemm_kernel<BM, BN, WM, WN><<<grid, T::NT, T::LDS_BYTES, s>>>(a);
     return hipGetLastError();
 }

@@ -106,7 +106,8 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     // 256-wide tiles take 128 KB of LDS (one workgroup per CU); 128x128 tiles take 64 KB
     const int per_cu = (p.tile_cfg == kTile128x128w4) ? 2 : 1;
     p.slots = (int64_t)dev.cus * per_cu;
-    if (p.tiles < p.slots && kt_total > 1) {
+    // only the smaller tiles carry the split fixup
+    if (p.tiles < p.slots && kt_total > 1 && p.tile_cfg == kTile128x128w4) {
         // split K over the idle slots; pieces are summed in K order by the last arriver. Each
         // piece keeps at least kMinPieceSteps k-steps: the last arriver reads every other piece's
         // float32 tile (BM*BN*4 bytes each), which costs more than a few k-steps of MFMA work.
