@@ -120,6 +120,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
             s.strips = p.strips;
             s.ks = p.ks;
             s.grid = (int)p.grid;
+            s.split = glk::make_unit_split(p.strips * p.ks, (int)p.grid);
             s.nxcd = p.nxcd;
             s.ws = ds.ws;
             s.counters = ds.counters;

@@ -74,13 +74,11 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // ---- this workgroup's units: [u_begin, u_end) of the strip-major (strip, stage) list -------
-    const int64_t U = (int64_t)p.strips * p.ks;
+    // ---- this workgroup's units: [u_begin, u_begin + nunits) of the strip-major list ----------
     const int w = xcd_remap((int)blockIdx.x, p.grid, p.nxcd);  // logical id: contiguous per XCD
-    const int64_t u_begin = (int64_t)w * U / p.grid;
-    const int64_t u_end = (int64_t)(w + 1) * U / p.grid;
-    const int nunits = (int)(u_end - u_begin);
-    const int first_strip = (int)(u_begin / p.ks);
+    const int u_begin = range_begin(p.split, w);
+    const int nunits = range_begin(p.split, w + 1) - u_begin;
+    const int first_strip = (int)((uint32_t)u_begin / (uint32_t)p.ks);
 
     // ---- load addressing ---------------------------------------------------------------------
     // B: wave w fetches rows 16w .. 16w+15 of a stage, 4 rows per instruction; lane l lands at
@@ -113,7 +111,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     // range read nothing: a zero-length descriptor). Units are issued in order, so the (strip,
     // stage) position advances by one each call instead of being divided out of the index.
     int iss_strip = first_strip;
-    int iss_stage = (int)(u_begin - (int64_t)first_strip * p.ks);
+    int iss_stage = u_begin - first_strip * p.ks;
     auto issue_unit = [&](int i) {
         char* st = lds + (i % STAGES) * T::STAGE_BYTES;
         const int strip = __builtin_amdgcn_readfirstlane(iss_strip);  // wave-uniform
@@ -209,13 +207,10 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     auto slot_off = [&](int wg, int seg, int t, int mt) {
         return (uint32_t)((((((wg * 2 + seg) * 4 + wave) * 2 + t) * MT + mt) * 64 + lane) * 16);
     };
-    auto wg_of_unit = [&](int64_t u) { return (int)(((u + 1) * p.grid - 1) / U); };
-    auto first_unit_of = [&](int wg) { return (int64_t)wg * U / p.grid; };
-
     // pieces of `strip` belong to logical workgroups wf .. wl (in K order)
     auto pieces_of = [&](int strip, int& wf, int& wl) {
-        wf = wg_of_unit((int64_t)strip * p.ks);
-        wl = wg_of_unit((int64_t)(strip + 1) * p.ks - 1);
+        wf = range_of(p.split, strip * p.ks);
+        wl = range_of(p.split, (strip + 1) * p.ks - 1);
     };
     auto store_partial = [&](int strip) {  // device scope; not waited for here
         const int seg = (strip == first_strip) ? 0 : 1;
@@ -243,7 +238,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
         if (tid == 0) counter_reset(&p.counters[strip]);
         // a piece's slot: pieces after the first start their range inside the strip (slot 0);
         // the first piece's range starts there too only if it starts at the strip's first unit
-        const int seg_first = (first_unit_of(wf) == (int64_t)strip * p.ks) ? 0 : 1;
+        const int seg_first = (range_begin(p.split, wf) == strip * p.ks) ? 0 : 1;
         constexpr int PB = 16 / MT;
         f32x4 sum[2][MT];
 #pragma unroll
@@ -290,7 +285,9 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     int red0 = -1, red1 = -1;    // strips this workgroup completes
     int cur_strip = first_strip;  // (strip, stage) of unit i
     int cur_stage = iss_stage;
-#pragma unroll
+    // kept rolled: unrolled, the compiler computes every prologue unit's addresses before the
+    // first load goes out
+#pragma unroll 1
     for (int i = 0; i < STAGES - 1; ++i) issue_unit(i);
     for (int i = 0; i < nunits; ++i) {
         wait_vmcnt<T::LOADS * (STAGES - 2)>();  // this wave's loads for unit i have landed
@@ -308,9 +305,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
             ++cur_strip;
         }
         if (i == nunits - 1 || strip_end) {  // last unit of a strip in this range
-            int wf, wl;
-            pieces_of(strip, wf, wl);
-            if (wf == wl) {  // the whole strip is ours
+            if (strip * p.ks >= u_begin && (strip + 1) * p.ks <= u_begin + nunits) {  // all ours
                 store_c(strip);
             } else {
                 store_partial(strip);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "stream_k.h"
+
 namespace glk {
 
 // ---- large-tile MFMA GEMM -------------------------------------------------------------------
@@ -57,8 +59,9 @@ struct SkinnyArgs {
     int lda, ldb, ldc;
     int strips;          // column strips of B (kSkinnyStrip columns each)
     int ks;              // 64-row stages per strip, ceil(K / 64)
-    int grid;            // workgroups; logical workgroup w takes units [w U / grid, (w+1) U / grid)
-                         // of the strip-major list of U = strips * ks (strip, stage) units
+    int grid;            // workgroups; logical workgroup w takes range w of `split`
+    UnitSplit split;     // grid balanced ranges of the strip-major list of U = strips * ks
+                         // (strip, stage) units, U < 2^31
     int nxcd;            // XCDs the hardware deals workgroups over; logical ids are contiguous per
                          // XCD, so the pieces of a strip meet in one XCD (1 = no remap)
     float* ws;           // 2 * grid * skinny_slot_floats(mtiles) floats

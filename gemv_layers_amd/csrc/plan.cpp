@@ -155,7 +155,9 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast
         p.reason = "alignment, leading dimension or size outside the fast kernels";
         return p;
     }
-    const bool skinny = (force == 1) || (force == 0 && M <= 64);
+    // the skinny kernel counts its (strip, stage) units in 32 bits
+    const bool units_fit = cdiv(N, kSkinnyStrip) * cdiv(K, kSkinnyStage) <= INT32_MAX;
+    const bool skinny = units_fit && ((force == 1) || (force == 0 && M <= 64));
     return skinny ? plan_skinny(M, N, K, dev) : plan_tile(M, N, K, dev);
 }
 

@@ -26,9 +26,9 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 TILE_SOURCES = ("gemv_layers_amd/csrc/gemm_tile.hip", "gemv_layers_amd/csrc/common.h",
-                "gemv_layers_amd/csrc/kernels.h")
+                "gemv_layers_amd/csrc/kernels.h", "gemv_layers_amd/csrc/stream_k.h")
 SKINNY_SOURCES = ("gemv_layers_amd/csrc/gemm_skinny.hip", "gemv_layers_amd/csrc/common.h",
-                  "gemv_layers_amd/csrc/kernels.h")
+                  "gemv_layers_amd/csrc/kernels.h", "gemv_layers_amd/csrc/stream_k.h")
 COPY_KERNEL = r"peak_copy_kernel"
 
 
