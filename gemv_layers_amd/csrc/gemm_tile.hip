@@ -11,14 +11,16 @@
 //   round-robin share of the grid is a contiguous run of tiles, then walked in grouped order
 //   (group_m tile rows at a time), so the tiles resident on one XCD share A rows and B columns
 //   in that XCD's L2.
-// * K advances in steps of BK = 32 through an LDS ring of STAGES stages (all of LDS). A stage's A
-//   tile (BM x 32) and B tile (32 x BN) are copied HBM -> LDS by direct-to-LDS buffer loads (1 KB
-//   per wave instruction, no registers), STAGES - 1 steps ahead of use; one barrier per step, with
-//   no memory fence, so the later stages' loads stay in flight.
+// * K advances in steps of BK = 32. A and B are copied HBM -> LDS by direct-to-LDS buffer loads
+//   (1 KB per wave instruction, no registers) into two rings that together fill LDS: B in stages of
+//   32 x BN, A in stages of BM x 64 so that every A row the loads touch is one whole 128-byte
+//   line (32-k stages would fetch half lines, which costs the address unit about a third more per
+//   byte). Each step every wave issues the same loads: half an A stage and one B stage, several
+//   steps ahead of use; one barrier per step, with no memory fence, so later loads stay in flight.
 // * MFMA operands are double-buffered in registers: while the matrix cores run step i from one
 //   register set, the LDS reads for step i + 1 fill the other, so the MFMA stream never waits on
 //   an LDS read; each barrier therefore guards the data of the step after the next.
-// * A sits in LDS K-contiguous (64-byte rows, 16-byte chunks stored at chunk ^ ((row >> 2) & 3))
+// * A sits in LDS K-contiguous (128-byte rows, 16-byte chunks stored at chunk ^ ((row >> 1) & 7))
 //   and is read with ds_read_b128. B stays row-major (N-contiguous, 32-byte column groups stored
 //   at group ^ (k & 7)); its MFMA operand, 8 consecutive k for one column, comes from
 //   ds_read_b64_tr_b16, which transposes 4 x 16 blocks on the way out of LDS.
@@ -40,26 +42,32 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int BM, int BN, int WM, int WN>
 struct TileTraits {
-    static constexpr int BK = 32;
-    // ring depth: all 160 KB of LDS for a one-workgroup-per-CU tile, half of it otherwise
-    static constexpr int STAGES = ((BM * BN >= 256 * 256) ? 163840 : 81920) / ((BM + BN) * BK * 2);
+    static constexpr int BK = 32;                           // k per step (B stage, MFMA step)
+    static constexpr int AK = 64;                           // k per A stage: 128-byte rows
+    // A ring SA stages of BM x 64, B ring SB stages of 32 x BN: all 160 KB of LDS for a
+    // one-workgroup-per-CU tile, half of it otherwise
+    static constexpr int SA = 3;
+    static constexpr int SB = 4;
+    static constexpr int DB = SB;                           // steps B is issued ahead
+    static constexpr int DA = DB + 1;                       // A half stages issued ahead
     static constexpr int NW = WM * WN;
     static constexpr int NT = NW * 64;
     static constexpr int WTM = BM / WM;
     static constexpr int WTN = BN / WN;
     static constexpr int TM = WTM / 32;
     static constexpr int TN = WTN / 32;
-    static constexpr int A_BYTES = BM * BK * 2;             // 64-byte rows
-    static constexpr int B_BYTES = BK * BN * 2;             // 2*BN-byte rows
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int A_BYTES = BM * AK * 2;             // one A stage, 128-byte rows
+    static constexpr int B_BYTES = BK * BN * 2;             // one B stage, 2*BN-byte rows
     static constexpr int A_INSTR = A_BYTES / 1024;          // 1 KB direct-to-LDS instructions
     static constexpr int B_INSTR = B_BYTES / 1024;
-    static constexpr int A_PER_WAVE = A_INSTR / NW;
+    static constexpr int A_PER_WAVE = A_INSTR / NW;         // per wave per A stage
+    static constexpr int A_HALF = A_PER_WAVE / 2;           // ... issued over two steps
     static constexpr int B_PER_WAVE = B_INSTR / NW;
-    static constexpr int LOADS = A_PER_WAVE + B_PER_WAVE;   // per wave per stage
+    static constexpr int LOADS = A_HALF + B_PER_WAVE;       // per wave per step
     static constexpr int B_CHUNKS = BN / 8;                 // 16-byte chunks per B row
     static constexpr int B_ROWS_PER_INSTR = 1024 / (2 * BN);
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int B_RING = SA * A_BYTES;             // B ring offset
+    static constexpr int LDS_BYTES = SA * A_BYTES + SB * B_BYTES;
     // The planner splits K only for tiles smaller than 256 x 256 (a grid of 256-wide tiles too
     // small to fill the card falls back to smaller tiles first), so only those carry the split
     // fixup, whose registers would otherwise crowd the main loop of the big tiles.
@@ -67,15 +75,16 @@ struct TileTraits {
     static_assert(A_PER_WAVE * NW == A_INSTR && B_PER_WAVE * NW == B_INSTR, "loads split evenly");
     static_assert(BN >= 128, "B swizzle needs at least 8 column groups per row");
     static_assert(TM >= 1 && TN >= 1, "wave tile must hold whole 32x32 MFMA tiles");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-    static_assert(STAGES >= 4, "ring depth");
-    static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
+    static_assert(A_HALF * 2 == A_PER_WAVE, "A stage loads split over two steps");
+    static_assert(LDS_BYTES <= ((BM * BN >= 256 * 256) ? 160 * 1024 : 80 * 1024), "LDS");
+    static_assert(DB <= SB && DA <= 2 * SA - 1, "ring slots reused only after their last read");
+    static_assert(LOADS * (DB + 2) + A_HALF <= 63, "vmcnt range");
 };
 
-// A: physical 16-byte chunk of logical chunk c (0..3) in row m. Sixteen consecutive rows (the
+// A: physical 16-byte chunk of logical chunk c (0..7) in row m. Sixteen consecutive rows (the
 // lanes one LDS cycle serves a ds_read_b128 for) then cover all 64 banks for any fixed c: the
-// four rows of a 256-byte bank line differ in m & 3, the four lines in (m >> 2) & 3.
-__device__ __forceinline__ int a_swz(int c, int m) { return c ^ ((m >> 2) & 3); }
+// two rows of a 256-byte bank line differ in m & 1, the eight lines in (m >> 1) & 7.
+__device__ __forceinline__ int a_swz(int c, int m) { return c ^ ((m >> 1) & 7); }
 // B: physical 32-byte column group of logical group u in k row k
 __device__ __forceinline__ int b_swz(int u, int k) { return u ^ (k & 7); }
 
@@ -84,7 +93,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN
                                amdgpu_waves_per_eu(1, 1)))
 tile_gemm_kernel(TileArgs p) {
     using T = TileTraits<BM, BN, WM, WN>;
-    constexpr int BK = T::BK, STAGES = T::STAGES, TM = T::TM, TN = T::TN;
+    constexpr int BK = T::BK, TM = T::TM, TN = T::TN;
     extern __shared__ __attribute__((aligned(1024))) char lds[];
 
     const int tid = threadIdx.x;
@@ -118,15 +127,17 @@ tile_gemm_kernel(TileArgs p) {
     const int nsteps = max(kt_end - kt_begin, 0);
 
     // ---- direct-to-LDS load addressing ---------------------------------------------------------
-    // A instruction i of this wave: tile rows 16 (wave * A_PER_WAVE + i) .. +15; lane l lands at
-    // byte 16 l = row + l/4, physical chunk l%4, and fetches the logical chunk stored there.
+    // A instruction i of this wave (per A stage): tile rows 8 (wave * A_PER_WAVE + i) .. +7; lane
+    // l lands at byte 16 l = row + l/8, physical chunk l%8, and fetches the logical chunk stored
+    // there. Instructions 0 .. A_HALF-1 go out in the first step of the stage's issue, the rest in
+    // the second.
     uint32_t a_off[T::A_PER_WAVE];
     int a_kchunk[T::A_PER_WAVE];
     bool a_row_ok[T::A_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < T::A_PER_WAVE; ++i) {
-        const int row = 16 * (wave * T::A_PER_WAVE + i) + (lane >> 2);
-        a_kchunk[i] = a_swz(lane & 3, row);  // the swizzle is an involution
+        const int row = 8 * (wave * T::A_PER_WAVE + i) + (lane >> 3);
+        a_kchunk[i] = a_swz(lane & 7, row);  // the swizzle is an involution
         a_row_ok[i] = m0 + row < p.M;
         a_off[i] = (uint32_t)(row * p.lda + 8 * a_kchunk[i]) * 2u;
     }
@@ -141,21 +152,34 @@ tile_gemm_kernel(TileArgs p) {
         b_off[i] = sel_off(n0 + col < p.N, (uint32_t)(k * p.ldb + col) * 2u);
     }
 
-    auto issue_step = [&](int i) {  // i-th k step of this workgroup, into ring slot i % STAGES
-        char* st = lds + (i % STAGES) * T::STAGE_BYTES;
-        const uint32_t st_lds = lds_addr(st);
-        const int k0 = (kt_begin + i) * BK;
-        const int krows = (i < nsteps) ? min(BK, p.K - k0) : 0;  // uniform
+    // half h of A stage s (k 64 s .. 64 s + 63 of this workgroup's range) into A slot s % SA
+    auto issue_a_half = [&](int s, int h) {
+        const uint32_t st_lds = lds_addr(lds + (s % T::SA) * T::A_BYTES);
+        const int k0 = kt_begin * BK + s * T::AK;
+        const int kend = kt_end * BK < p.K ? kt_end * BK : p.K;
+        const int krows = max(0, min(T::AK, kend - k0));  // uniform
         const i32x4 ar = rsrc_words(p.A + (size_t)m0 * p.lda + k0, kBufRecords);
 #pragma unroll
-        for (int t = 0; t < T::A_PER_WAVE; ++t) {
+        for (int u = 0; u < T::A_HALF; ++u) {
+            const int t = h * T::A_HALF + u;
             const bool ok = a_row_ok[t] && 8 * a_kchunk[t] < krows;
             dma16(ar, st_lds + (wave * T::A_PER_WAVE + t) * 1024, sel_off(ok, a_off[t]));
         }
+    };
+    // the B stage of step i into B slot i % SB
+    auto issue_b = [&](int i) {
+        const uint32_t st_lds = lds_addr(lds + T::B_RING + (i % T::SB) * T::B_BYTES);
+        const int k0 = (kt_begin + i) * BK;
+        const int krows = (i < nsteps) ? min(BK, p.K - k0) : 0;  // uniform
         const i32x4 br = rsrc_words(p.B + (size_t)k0 * p.ldb + n0, (uint32_t)krows * (uint32_t)p.ldb * 2u);
 #pragma unroll
         for (int t = 0; t < T::B_PER_WAVE; ++t)
-            dma16(br, st_lds + T::A_BYTES + (wave * T::B_PER_WAVE + t) * 1024, b_off[t]);
+            dma16(br, st_lds + (wave * T::B_PER_WAVE + t) * 1024, b_off[t]);
+    };
+    // the loads of loop iteration I: A half stage I + DA, then the B stage of step I + DB
+    auto issue_iter = [&](int I) {
+        issue_a_half((I + T::DA) >> 1, (I + T::DA) & 1);
+        issue_b(I + T::DB);
     };
 
     f32x16 acc[TN][TM];
@@ -180,14 +204,15 @@ tile_gemm_kernel(TileArgs p) {
     };
 
     auto read_frags = [&](int i, Frags& f) {
-        const char* st = lds + (i % STAGES) * T::STAGE_BYTES;
-        const char* sb = st + T::A_BYTES;
+        const char* sa = lds + ((i >> 1) % T::SA) * T::A_BYTES;
+        const char* sb = lds + T::B_RING + (i % T::SB) * T::B_BYTES;
+        const int ah = 4 * (i & 1);  // the step's k half of the A stage: chunks ah .. ah + 3
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
 #pragma unroll
             for (int mi = 0; mi < TM; ++mi) {
                 const int m = wm * T::WTM + mi * 32 + fa_row;
-                f.a[kk][mi] = *reinterpret_cast<const bf16x8*>(st + m * 64 + 16 * a_swz(2 * kk + fa_half, m));
+                f.a[kk][mi] = *reinterpret_cast<const bf16x8*>(sa + m * 128 + 16 * a_swz(ah + 2 * kk + fa_half, m));
             }
 #pragma unroll
             for (int ni = 0; ni < TN; ++ni) {
@@ -215,23 +240,30 @@ tile_gemm_kernel(TileArgs p) {
     };
 
     // ---- main loop ------------------------------------------------------------------------
-    // Before step i's MFMAs: its fragments are in registers (read during step i - 1), step i + 1
-    // is in LDS and visible, steps i + 2 .. i + STAGES - 1 are in flight.
+    // Iteration I issues A half stage I + DA and the B stage of step I + DB, reads the fragments
+    // of step I + 1 and runs the MFMAs of step I (fragments read during iteration I - 1). Every
+    // iteration's loads are the same LOADS instructions per wave, so "the loads of iteration X
+    // have landed" is one vmcnt threshold: step I + 1's B stage was issued in iteration
+    // I + 1 - DB and the second half of its A stage no later, so iteration I waits for all but
+    // the last DB - 2 iterations' loads. A B slot is refilled DB steps after the step that last
+    // read it, an A slot 2 SA - DA half stages after; both reads ended before that iteration's
+    // barrier.
     Frags f0, f1;
+    issue_a_half(0, 0);  // the prologue issues as iterations -DB .. -1 would, plus half stage 0
 #pragma unroll
-    for (int i = 0; i < STAGES - 1; ++i) issue_step(i);
-    wait_vmcnt<T::LOADS * (STAGES - 2)>();
+    for (int I = -T::DB; I < 0; ++I) issue_iter(I);
+    wait_vmcnt<T::LOADS * (T::DB - 1)>();  // iteration -DB's loads (step 0's B, A stage 0) landed
     lds_barrier();
     read_frags(0, f0);
     // (reading the next fragments past the last step is harmless: that slot holds zeros or
     // stale data that no MFMA consumes)
-#define GLK_TILE_STEP(I, CUR, NEXT)                                                          \
-    do {                                                                                     \
-        wait_vmcnt<T::LOADS * (STAGES - 3)>(); /* this wave's loads for step I + 1 landed */ \
-        lds_barrier(); /* every wave's have; all are done reading slot (I - 1) % STAGES */   \
-        issue_step((I) + STAGES - 1);          /* refills that slot */                       \
-        read_frags((I) + 1, NEXT);                                                           \
-        mfma_frags(CUR);                                                                     \
+#define GLK_TILE_STEP(I, CUR, NEXT)                                                           \
+    do {                                                                                      \
+        wait_vmcnt<T::LOADS * (T::DB - 2)>(); /* this wave's loads for step I + 1 landed */   \
+        lds_barrier(); /* every wave's have; all are done reading the slots refilled next */  \
+        issue_iter(I);                                                                        \
+        read_frags((I) + 1, NEXT);                                                            \
+        mfma_frags(CUR);                                                                      \
     } while (0)
     int i = 0;
     for (; i + 1 < nsteps; i += 2) {
