@@ -28,6 +28,7 @@ EXPORTS = (
     "gemm_init", "gemm_bf16", "gemm_bf16_skinny", "gemm_bf16_tiled", "gemm_plan_describe",
     "gemm_wave_efficiency", "gemm_last_plan", "gemm_status_string", "gemm_finalize",
     "gemm_peak_mfma_launch", "gemm_peak_copy_launch", "gemm_peak_read_launch",
+    "gemm_peak_clock_launch",
     "gemm_peak_empty_launch", "gemm_fill_launch",
 )
 
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_peak_copy_launch.restype = i32
     L.gemm_peak_read_launch.argtypes = [p, i64, p, p]
     L.gemm_peak_read_launch.restype = i32
+    L.gemm_peak_clock_launch.argtypes = [i64, i32, p, p]
+    L.gemm_peak_clock_launch.restype = i32
     L.gemm_peak_empty_launch.argtypes = [p]
     L.gemm_peak_empty_launch.restype = i32
     L.gemm_fill_launch.argtypes = [p, i64, u32, p]
@@ -149,6 +152,10 @@ def gemm_peak_copy_launch(src, dst, nbytes, stream=None) -> None:
 
 def gemm_peak_read_launch(src, nbytes, sink, stream=None) -> None:
     _check("gemm_peak_read_launch", lib().gemm_peak_read_launch(src, nbytes, sink, stream))
+
+
+def gemm_peak_clock_launch(iters, blocks, out, stream=None) -> None:
+    _check("gemm_peak_clock_launch", lib().gemm_peak_clock_launch(iters, blocks, out, stream))
 
 
 def gemm_peak_empty_launch(stream=None) -> None:

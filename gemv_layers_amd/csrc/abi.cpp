@@ -282,6 +282,13 @@ int gemm_peak_read_launch(const void* src, int64_t bytes, uint32_t* sink, gemm_s
                : GEMM_ERR_HIP;
 }
 
+int gemm_peak_clock_launch(int64_t iters, int blocks, uint64_t* out, gemm_stream_t stream) {
+    if (iters < 0 || blocks <= 0 || !out) return GEMM_ERR_INVALID_ARG;
+    return glk::launch_peak_clock(iters, blocks, out, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
 int gemm_peak_empty_launch(gemm_stream_t stream) {
     return glk::launch_peak_empty(reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? GEMM_OK
                                                                                        : GEMM_ERR_HIP;

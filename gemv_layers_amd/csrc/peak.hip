@@ -93,6 +93,23 @@ __global__ void __launch_bounds__(256) peak_read_kernel(const u32x4* __restrict_
 
 __global__ void peak_empty_kernel() {}
 
+// Shader-clock probe: wave 0 of each workgroup reads the core-clock counter (s_memtime) and the
+// 100 MHz constant counter (s_memrealtime) around a dependent FMA chain. Power management moves
+// the clock over milliseconds, so a probe enqueued right behind a stream of kernels reads the
+// clock the card held under that load.
+__global__ void __launch_bounds__(64) peak_clock_kernel(int64_t iters, uint64_t* out) {
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    float x = (float)threadIdx.x;
+    for (int64_t i = 0; i < iters; ++i) x = __builtin_fmaf(x, 0.999f, 0.5f);
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        out[2 * (size_t)blockIdx.x] = t1 - t0;
+        out[2 * (size_t)blockIdx.x + 1] = (x == -1.0f) ? 0 : r1 - r0;  // x kept alive
+    }
+}
+
 hipError_t launch_peak_mfma(int64_t iters, int blocks, float* sink, uint64_t* cycles, hipStream_t s) {
     peak_mfma_kernel<<<blocks, 256, 0, s>>>(iters, sink, cycles);
     return hipGetLastError();
@@ -115,6 +132,11 @@ hipError_t launch_peak_copy(const void* src, void* dst, int64_t bytes, hipStream
 hipError_t launch_peak_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s) {
     const int64_t n16 = bytes / 16;
     peak_read_kernel<<<stream_blocks(n16), 256, 0, s>>>(static_cast<const u32x4*>(src), n16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_peak_clock(int64_t iters, int blocks, uint64_t* out, hipStream_t s) {
+    peak_clock_kernel<<<blocks, 64, 0, s>>>(iters, out);
     return hipGetLastError();
 }
 

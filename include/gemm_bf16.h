@@ -151,6 +151,15 @@ int gemm_peak_read_launch(const void *src, int64_t bytes, uint32_t *sink, gemm_s
 /* gemm_peak_empty_launch: one workgroup that does nothing (launch floor). */
 int gemm_peak_empty_launch(gemm_stream_t stream);
 
+/*
+ * gemm_peak_clock_launch: `blocks` workgroups of one wave each run `iters` dependent fp32 FMAs;
+ * `out` (device, >= 2 * blocks uint64) receives, per block, the s_memtime delta (shader clock
+ * cycles) and the s_memrealtime delta (100 MHz constant clock) around the loop. Enqueued right
+ * after other work on the same stream it reads the shader clock the card held under that work
+ * (the clock changes over milliseconds, the probe lasts microseconds).
+ */
+int gemm_peak_clock_launch(int64_t iters, int blocks, uint64_t *out, gemm_stream_t stream);
+
 /* gemm_fill_launch: writes the 32-bit `value` over dst[0 .. bytes) (bytes % 4 == 0); used to
  * evict the device's caches between timed calls and to poison outputs before checks. */
 int gemm_fill_launch(void *dst, int64_t bytes, uint32_t value, gemm_stream_t stream);

@@ -312,7 +312,13 @@ def test_measurement_kernels_run_and_copy_is_exact():
     cyc = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
     g.gemm_peak_mfma_launch(1000, blocks, ctypes.c_void_p(fs.data_ptr()),
                             ctypes.c_void_p(cyc.data_ptr()), s)
+    clk = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    g.gemm_peak_clock_launch(2000, blocks, ctypes.c_void_p(clk.data_ptr()), s)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
     assert torch.all(cyc > 0)
     assert torch.isfinite(fs).all()
+    c = clk.view(-1, 2).double().cpu()
+    assert torch.all(c > 0)
+    ghz = c[:, 0] / c[:, 1] * 0.1  # s_memrealtime ticks at 100 MHz
+    assert 0.3 < float(ghz.median()) < 3.0
