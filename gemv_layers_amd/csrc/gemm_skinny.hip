@@ -212,12 +212,16 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
         wf = range_of(p.split, strip * p.ks);
         wl = range_of(p.split, (strip + 1) * p.ks - 1);
     };
+    // Only lanes holding a row below M move data: the padding rows' lanes get an out-of-range
+    // offset, so a piece costs M rows of traffic rather than 16 MT.
+    const int part_row = lane & 15;
     auto store_partial = [&](int strip) {  // device scope; not waited for here
         const int seg = (strip == first_strip) ? 0 : 1;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) buf_store16_dev(ws, slot_off(w, seg, t, mt), f4_bits(acc[t][mt]));
+            for (int mt = 0; mt < MT; ++mt)
+                buf_store16_dev(ws, sel_off(16 * mt + part_row < p.M, slot_off(w, seg, t, mt)), f4_bits(acc[t][mt]));
     };
     // once every wave's partial stores of `strip` have completed: count this piece in; true for
     // the piece that completes the strip
@@ -255,7 +259,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
-                        const uint32_t off = sel_off(wg <= wl, slot_off(wg, sq, t, mt));
+                        const uint32_t off = sel_off(wg <= wl && 16 * mt + part_row < p.M, slot_off(wg, sq, t, mt));
                         v[q][t][mt] = bits_f4(buf_load16_dev(ws, off));
                     }
             }
