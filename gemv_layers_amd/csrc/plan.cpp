@@ -46,6 +46,23 @@ bool fast_path_ok(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, c
 
 static void finish_waves(Plan& p) { wave_efficiency(p.grid, p.slots, &p.wave_eff, &p.waves); }
 
+// The split of the strip-major list of (strip, stage) units into `grid` balanced ranges puts
+// every range boundary on a strip boundary whenever grid = strips * S: each workgroup then holds
+// one piece of one strip, and a strip has exactly S pieces (S = 1: no partials at all), so no
+// piece ends mid-range and the fixup is as short as it gets. The planner takes such an aligned
+// grid, with the most pieces per strip that fit one wave of workgroups, when it occupies enough
+// of the CUs: two thirds for up to two 16-row tiles of M, all but a sixteenth above that (wider
+// M does more work per byte and wants every CU). Otherwise Stream-K ranges over one workgroup per
+// CU cut the strips wherever they fall.
+static int64_t skinny_grid(int strips, int ks, int mtiles, int cus) {
+    const int64_t units = (int64_t)strips * ks;
+    const int64_t s = std::min<int64_t>(cus / strips, ks);
+    const int64_t aligned = (int64_t)strips * s;
+    const bool enough = (mtiles <= 2) ? 3 * aligned >= 2 * (int64_t)cus : 16 * aligned >= 15 * (int64_t)cus;
+    if (s >= 1 && enough) return aligned;
+    return std::min<int64_t>(units, cus);
+}
+
 static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     Plan p;
     p.kernel = kKernSkinny;
@@ -55,9 +72,9 @@ static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) 
     p.strips = (int)cdiv(N, kSkinnyStrip);
     p.ks = (int)cdiv(K, kSkinnyStage);
     const int64_t units = (int64_t)p.strips * p.ks;
-    // one workgroup per CU (the LDS ring takes ~128 KB), each with a balanced range of units
+    // one workgroup per CU at most (the LDS ring takes ~128 KB)
     p.slots = dev.cus;
-    p.grid = std::min<int64_t>(units, dev.cus);
+    p.grid = skinny_grid(p.strips, p.ks, p.mtiles, dev.cus);
     const int64_t slot_floats = skinny_slot_floats(p.mtiles);
     // two partial slots per workgroup; fall back to one unit range per strip (no partials) if
     // the workspace or the counters cannot hold them
@@ -67,7 +84,9 @@ static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) 
     p.splits = (int)cdiv(p.grid, p.strips);  // pieces per strip, about
     finish_waves(p);
     p.reason = "M <= 64: weights streamed once, " + std::to_string(p.grid) +
-               " workgroups over " + std::to_string(units) + " strip stages";
+               ((p.grid % p.strips == 0) ? " workgroups, each one piece of one strip, over "
+                                         : " workgroups over ") +
+               std::to_string(units) + " strip stages";
     return p;
 }
 

@@ -105,11 +105,12 @@ def test_skinny_kernel_float_and_exact(M, N, K):
     check_exact(run("skinny", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"skinny int {M}x{N}x{K}")
 
 
-# Stream-K ranges of the skinny kernel that cross strip boundaries (strip counts that do not
-# divide the grid): short ranges, where a strip's piece is announced at the range's end, and long
-# ones, where a strip ending early in a range is announced mid-stream; ragged N and K included.
-STREAMK_SHAPES = [(3, 128 * 9 + 8, 64 * 37 + 8), (1, 128 * 7, 64 * 400), (2, 128 * 13, 64 * 170 + 24),
-                  (33, 128 * 11, 12872), (64, 128 * 9, 64 * 300)]
+# Stream-K ranges of the skinny kernel that cross strip boundaries: with 129..170 strips (or, for
+# three or more 16-row tiles of M, any count whose aligned grid leaves a sixteenth of the CUs
+# idle) 256 ranges cut the strips wherever they fall. A range may end inside a strip (announced at the range's end)
+# or contain a strip's end (announced mid-stream); ragged N and K included.
+STREAMK_SHAPES = [(3, 128 * 141 + 8, 64 * 37 + 8), (1, 128 * 150, 64 * 40), (2, 128 * 135 + 24, 64 * 33 + 24),
+                  (33, 128 * 131, 2056), (64, 128 * 145, 64 * 16)]
 
 
 @pytest.mark.parametrize("M,N,K", STREAMK_SHAPES)
@@ -125,6 +126,25 @@ def test_skinny_stream_k_boundaries(M, N, K):
     check_float(run("skinny", A, B, M, N, K), A, B, M, N, K, f"skinny {M}x{N}x{K}")
     Ai = matrix("int", M, K, seed=7100 + M)
     Bi = matrix("int", K, N, seed=8100 + N)
+    check_exact(run("skinny", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"skinny int {M}x{N}x{K}")
+
+
+# Aligned layouts (grid = strips x pieces, every range one piece of one strip): few pieces on
+# two thirds of the CUs, and strips cut into many pieces (long fixups in batches), for one to four
+# 16-row tiles of M.
+ALIGNED_SHAPES = [(1, 128 * 65, 4096), (5, 128 * 65 + 8, 1000), (64, 128 * 9, 64 * 300), (1, 128 * 7, 64 * 400),
+                  (17, 128 * 7 + 40, 64 * 300 + 8), (40, 128 * 11, 12872)]
+
+
+@pytest.mark.parametrize("M,N,K", ALIGNED_SHAPES)
+def test_skinny_aligned_layouts(M, N, K):
+    plan = g.gemm_plan_describe(M, N, K, 256, 1)
+    assert plan["kernel"] == "skinny" and plan["grid"] % plan["strips"] == 0
+    A = matrix("normal", M, K, seed=5200 + M)
+    B = matrix("normal", K, N, seed=6200 + N, sigma=0.02)
+    check_float(run("skinny", A, B, M, N, K), A, B, M, N, K, f"skinny {M}x{N}x{K}")
+    Ai = matrix("int", M, K, seed=7200 + M)
+    Bi = matrix("int", K, N, seed=8200 + N)
     check_exact(run("skinny", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"skinny int {M}x{N}x{K}")
 
 

@@ -90,8 +90,27 @@ def test_decode_shapes_stream_weights(name):
     assert p["mtiles"] == _cdiv(w.M, 16)
     assert p["strips"] == _cdiv(w.N, 128)
     assert p["ks"] == _cdiv(w.K, 64)
-    # one workgroup per CU, each with a balanced range of (strip, stage) units
-    assert p["grid"] == 256 and p["waves"] == 1 and p["wave_eff"] == 1.0
+    # at most one workgroup per CU: either every range is one piece of one strip on at least two
+    # thirds of the CUs, or Stream-K ranges over all of them
+    assert p["grid"] <= 256 and p["waves"] == 1
+    assert (p["grid"] % p["strips"] == 0 and 3 * p["grid"] >= 2 * 256) or p["grid"] == 256
+
+
+# (M, N, K) -> grid: an aligned grid (strips x the most pieces per strip that fit 256) when it
+# fills two thirds of the CUs (one or two 16-row tiles of M) or fifteen sixteenths (more rows);
+# else Stream-K ranges over min(units, 256) workgroups
+LAYOUTS = [((1, 4096, 11008), 256),       # 32 strips x 8 pieces
+           ((1, 11008, 4096), 172),       # 86 strips x 2 pieces: two thirds of the CUs
+           ((64, 11008, 4096), 256),      # the same 172 is too few for four tiles of M: Stream-K
+           ((1, 128 * 65, 4096), 195),    # 65 x 3
+           ((1, 18056, 4096), 256),       # 142 strips, 142 < 171: Stream-K
+           ((3, 256, 128), 4),            # 2 strips x 2 stages: one unit per workgroup
+           ((1, 4096, 64), 32)]           # one stage per strip
+
+
+@pytest.mark.parametrize("shape,want", LAYOUTS)
+def test_skinny_layout_choice(shape, want):
+    assert g.gemm_plan_describe(*shape, 256)["grid"] == want
 
 
 def test_skinny_small_problem_has_one_unit_per_workgroup():
