@@ -346,12 +346,38 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             b2b_us = e0.elapsed_time(e1) * 1e3 / nb
+            # the same calls replayed from a captured graph (one call per rotated copy), as a
+            # serving loop would: launch gaps between kernels shrink, the kernels are the same
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                call(Bs[0])
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(copies):
+                    g.gemm_bf16(wd.M, wd.N, wd.K, P(Ad), wd.K, P(Bs[i]), wd.N, P(Cd), wd.N,
+                                g.current_stream_handle())
+            graph.replay()
+            torch.cuda.synchronize()
+            reps = 8
+            e0, e1 = events(2)
+            e0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            graph_us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+            del graph
             single_us = float(np.median(singles))
             rec = {"us_single_median": round(single_us, 2),
                    "us_single_min": round(float(np.min(singles)), 2),
                    "us_back_to_back": round(b2b_us, 2),
                    "gbps_single": round(wd.bytes / (single_us * 1e-6) / 1e9, 1),
                    "gbps_back_to_back": round(wd.bytes / (b2b_us * 1e-6) / 1e9, 1),
+                   "us_graph_replay": round(graph_us, 2),
+                   "gbps_graph_replay": round(wd.bytes / (graph_us * 1e-6) / 1e9, 1),
                    "plan_splits": g.gemm_last_plan().get("splits")}
             if "hbm_copy_gbps" in peaks:
                 rec["frac_of_measured_copy"] = round(rec["gbps_back_to_back"] / peaks["hbm_copy_gbps"], 4)

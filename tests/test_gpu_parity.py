@@ -316,6 +316,51 @@ def test_many_back_to_back_calls_stay_correct():
         assert np.array_equal(host(C).reshape(M, N), want)
 
 
+# ---- graph capture ---------------------------------------------------------------------------
+# The kernels allocate nothing and need no memset: split counters return to zero inside the
+# kernel, so one captured call replays correctly any number of times. Each case mixes the
+# counter-using layouts (aligned split pieces, Stream-K ranges across strips, tile split-K);
+# between replays, eager work poisons the output and runs other shapes over the shared
+# workspace, and every replay must equal the eager result bit for bit.
+GRAPH_CASES = [("auto", 1, 4096, 11008), ("skinny", 3, 128 * 141 + 8, 64 * 37 + 8),
+               ("auto", 64, 11008, 4096), ("tiled", 1000, 1000, 1000)]
+
+
+@pytest.mark.parametrize("entry,M,N,K", GRAPH_CASES)
+def test_graph_replay_matches_eager(entry, M, N, K):
+    A = matrix("normal", M, K, seed=9100 + M)
+    B = matrix("normal", K, N, seed=9200 + N, sigma=0.02)
+    eager = run(entry, A, B, M, N, K)
+    check_float(eager, A, B, M, N, K, f"{entry} {M}x{N}x{K} eager")
+    dA, dB = dev(A), dev(B)
+    C = torch.empty(M * N, dtype=torch.bfloat16, device="cuda")
+    other = [(2, 8320, 4096), (300, 520, 328)]
+    oA = [dev(matrix("normal", m, k, seed=9300 + m)) for m, n, k in other]
+    oB = [dev(matrix("normal", k, n, seed=9400 + n)) for m, n, k in other]
+    oC = [torch.empty(m * n, dtype=torch.bfloat16, device="cuda") for m, n, k in other]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream, as capture expects
+        ENTRIES[entry](M, N, K, ctypes.c_void_p(dA.data_ptr()), K, ctypes.c_void_p(dB.data_ptr()), N,
+                       ctypes.c_void_p(C.data_ptr()), N, g.current_stream_handle())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ENTRIES[entry](M, N, K, ctypes.c_void_p(dA.data_ptr()), K, ctypes.c_void_p(dB.data_ptr()), N,
+                       ctypes.c_void_p(C.data_ptr()), N, g.current_stream_handle())
+    for rep in range(4):
+        g.gemm_fill_launch(ctypes.c_void_p(C.data_ptr()), C.numel() * 2, POISON)
+        (m, n, k), a, b, c = other[rep % 2], oA[rep % 2], oB[rep % 2], oC[rep % 2]
+        g.gemm_bf16(m, n, k, ctypes.c_void_p(a.data_ptr()), k, ctypes.c_void_p(b.data_ptr()), n,
+                    ctypes.c_void_p(c.data_ptr()), n, g.current_stream_handle())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host(C).reshape(M, N)
+        assert np.array_equal(got, eager), f"replay {rep} of {entry} {M}x{N}x{K} differs from eager"
+
+
 # ---- measurement kernels ---------------------------------------------------------------------
 
 def test_measurement_kernels_run_and_copy_is_exact():
