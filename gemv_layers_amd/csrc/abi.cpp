@@ -124,7 +124,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
             s.nxcd = p.nxcd;
             s.ws = ds.ws;
             s.counters = ds.counters;
-            e = glk::launch_skinny_gemm(p.mtiles, s, stream);
+            e = glk::launch_skinny_gemm(p.mtiles, p.strip, s, stream);
             break;
         }
         default:

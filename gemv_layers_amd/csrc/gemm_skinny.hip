@@ -8,21 +8,22 @@
 // slice leaving the workspace as it found it so a call stays one launch; enough bytes in flight
 // per workgroup to reach the memory floor):
 //
-// * The work is a strip-major list of units (one 64-row stage of one 128-column strip). Exactly one
-//   workgroup per CU takes a balanced, contiguous range of units (the Stream-K decomposition of
-//   the spark-kernels post, "stream-k proper"), so no partial last wave of workgroups exists; only
-//   the first and the last strip a range touches can be partial. Ranges are dealt so that each
+// * The work is a strip-major list of units (one 64-row stage of one strip of SW = 128 or 256
+//   columns). At most one workgroup per CU takes a balanced, contiguous range of units (the
+//   Stream-K decomposition of the spark-kernels post, "stream-k proper"), so no partial last wave
+//   of workgroups exists; only the first and the last strip a range touches can be partial, and
+//   when the grid is a whole number of pieces per strip every range is one piece of one strip. Ranges are dealt so that each
 //   XCD holds consecutive ones, so the pieces of a strip mostly run on one XCD and an XCD that
 //   starts late delays only its own strips. The units stream through
 //   an LDS ring of STAGES stages: each is fetched with direct-to-LDS buffer loads (16 bytes per
 //   lane, 1 KB per wave instruction, no registers involved), STAGES - 1 stages ahead of use, and
 //   carries the matching 64 columns of A (M rows) so every wave reads A from LDS.
-// * B sits in LDS row-major (k rows of 256 bytes). The MFMA operand wants 8 consecutive k per
+// * B sits in LDS row-major (k rows of 2 SW bytes). The MFMA operand wants 8 consecutive k per
 //   lane for one column, which ds_read_b64_tr_b16 produces directly from row-major data: within
 //   each 16-lane group, lanes 4r .. 4r+3 address row r of a 4 x 16 block and lane j receives
 //   column j. The 32-byte column groups of each row are XOR-swizzled with the row so the rows a
 //   wave reads together fall in different banks.
-// * Each of the 4 waves owns 32 columns (two 16-column MFMA tiles) for all M rows, using
+// * Each of the 4 waves owns SW / 4 columns (SW / 64 16-column MFMA tiles) for all M rows, using
 //   v_mfma_f32_16x16x32_bf16 with B as the first operand: each lane's accumulator then holds 4
 //   consecutive columns of one row of C, stored as one 8-byte bf16 write. M is padded to 16 per
 //   tile with zero rows (A rows past M are fetched as zeros); the matrix cores are otherwise idle
@@ -42,32 +43,44 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kSkRows = 64;                            // k rows per LDS stage
-constexpr int kSkRowBytes = kSkinnyStrip * 2;          // 256 bytes of B per row
-constexpr int kSkBBytes = kSkRows * kSkRowBytes;       // 16 KB of B per stage
+constexpr int kSkRows = kSkinnyStage;                  // k rows per LDS stage
 
-template <int MT>
+// MT 16-row tiles of M; SW columns per strip
+template <int MT, int SW>
 struct SkinnyTraits {
+    static constexpr int TN = SW / 64;                     // 16-column tiles per wave
+    static constexpr int ROW_BYTES = SW * 2;               // B bytes per k row of a strip
+    static constexpr int B_BYTES = kSkRows * ROW_BYTES;    // B bytes per stage (16 or 32 KB)
+    static constexpr int B_INSTR = B_BYTES / 1024;         // 1 KB load instructions for B per stage
+    static constexpr int B_PER_WAVE = B_INSTR / 4;
+    static constexpr int ROWS_PER_INSTR = 1024 / ROW_BYTES;
+    static constexpr int CHUNKS = ROW_BYTES / 16;          // 16-byte chunks per B row
     static constexpr int A_BYTES = 16 * MT * kSkRows * 2;  // A rows (M padded to 16 MT) x 64 k
-    static constexpr int STAGE_BYTES = kSkBBytes + A_BYTES;
-    static constexpr int STAGES = 131072 / STAGE_BYTES;    // ring in 128 KB: one workgroup per CU
+    static constexpr int STAGE_BYTES = B_BYTES + A_BYTES;
+    // ring: 128 KB for 128-column strips (measured no slower than all of LDS), all of LDS (less
+    // the padding sink and the static flag) for 256-column ones, whose stages are twice as big
+    static constexpr int STAGES = (SW == 128 ? 131072 : 163840 - 2048) / STAGE_BYTES;
     static constexpr int DUMMY = STAGES * STAGE_BYTES;     // 1 KB sink for padding loads
     static constexpr int LDS_BYTES = DUMMY + 1024;
     static constexpr int A_INSTR = A_BYTES / 1024;         // 1 KB load instructions for A per stage
     static constexpr int A_PER_WAVE = (A_INSTR + 3) / 4;
-    static constexpr int LOADS = 4 + A_PER_WAVE;           // load instructions per wave per stage
-    static constexpr int SLOT_FLOATS = 4 * 2 * MT * 64 * 4; // one piece: 4 waves x 2 tiles x M
+    static constexpr int LOADS = B_PER_WAVE + A_PER_WAVE;  // load instructions per wave per stage
+    static constexpr int SLOT_FLOATS = 4 * TN * MT * 64 * 4; // one piece: 4 waves x TN tiles x M
+    static_assert(SW == 128 || SW == 256, "strip width");
+    static_assert(B_PER_WAVE * ROWS_PER_INSTR == 16, "each wave loads 16 B rows of a stage");
     static_assert(STAGES >= 3, "need at least three stages");
     static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
 };
 
-// Physical 32-byte column group of logical group u in row r (8 groups of 16 columns per row):
-// the 4 rows a 16-lane group reads, and the groups 8 rows apart, land on different banks.
+// Physical 32-byte column group of logical group u in row r (8 or 16 groups of 16 columns per
+// row; rows are whole 256-byte bank lines, or two of them): the 4 rows a 16-lane group reads, and
+// the groups 8 rows apart, land on different banks.
 __device__ __forceinline__ int b_swz(int u, int r) { return u ^ ((r & 3) | (((r >> 3) & 1) << 2)); }
 
-template <int MT>
+template <int MT, int SW>
 __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
-    using T = SkinnyTraits<MT>;
+    using T = SkinnyTraits<MT, SW>;
+    constexpr int TN = T::TN;
     constexpr int STAGES = T::STAGES;
     extern __shared__ __attribute__((aligned(1024))) char lds[];
 
@@ -85,13 +98,14 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     // byte 16 l of the instruction's 1 KB = row 4i + l/16 (of the wave's 16), physical 16-byte
     // chunk l%16, and fetches the logical chunk the swizzle keeps there (the swizzle is an
     // involution on the group index). Column validity is checked per unit (the strip varies).
-    uint32_t b_off[4];  // byte offset from (stage row 0, strip column 0)
-    int b_col[4];
+    uint32_t b_off[T::B_PER_WAVE];
+    int b_col[T::B_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * i + (lane >> 4);
-        const int u = b_swz((lane & 15) >> 1, r);
-        b_col[i] = 16 * u + 8 * (lane & 1);
+    for (int i = 0; i < T::B_PER_WAVE; ++i) {
+        const int r = 16 * wave + T::ROWS_PER_INSTR * i + lane / T::CHUNKS;
+        const int pc = lane % T::CHUNKS;
+        const int u = b_swz(pc >> 1, r);
+        b_col[i] = 16 * u + 8 * (pc & 1);
         b_off[i] = (uint32_t)(r * p.ldb + b_col[i]) * 2u;
     }
     // A: instruction j (= wave + 4t) covers A rows 8j .. 8j+7 of the padded M x 64 block;
@@ -120,13 +134,13 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
             iss_stage = 0;
             ++iss_strip;
         }
-        const int n0 = strip * kSkinnyStrip;
+        const int n0 = strip * SW;
         const int rows = (i < nunits) ? min(kSkRows, p.K - k0) : 0;  // uniform
         const i32x4 b_rsrc = rsrc_words(p.B + (size_t)k0 * p.ldb + n0, (uint32_t)rows * (uint32_t)p.ldb * 2u);
         const uint32_t st_lds = lds_addr(st);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            dma16(b_rsrc, st_lds + (16 * wave + 4 * t) * kSkRowBytes, sel_off(n0 + b_col[t] < p.N, b_off[t]));
+        for (int t = 0; t < T::B_PER_WAVE; ++t)
+            dma16(b_rsrc, st_lds + (16 * wave + T::ROWS_PER_INSTR * t) * T::ROW_BYTES, sel_off(n0 + b_col[t] < p.N, b_off[t]));
         // A columns k0 .. k0 + rows; K % 8 == 0, so a 16-byte chunk is wholly in or out. A wave
         // without a real A instruction this round (the count need not divide by 4) still issues
         // one, into a spare kilobyte, so every wave issues the same number of loads per unit and
@@ -137,13 +151,13 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
             const int j = wave + 4 * t;
             const bool real = j < T::A_INSTR;
             const uint32_t off = sel_off(real && 8 * a_chunk[t] < rows, a_off[t]);
-            dma16(a_rsrc, real ? st_lds + kSkBBytes + j * 1024 : dummy_lds, off);
+            dma16(a_rsrc, real ? st_lds + T::B_BYTES + j * 1024 : dummy_lds, off);
         }
     };
 
-    f32x4 acc[2][MT];
+    f32x4 acc[TN][MT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < TN; ++t)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{};
 
@@ -159,15 +173,15 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
         const char* st = lds + (i % STAGES) * T::STAGE_BYTES;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {               // two 32-row blocks per stage
-            bf16x8 bx[2];
+            bf16x8 bx[TN];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int u = 2 * wave + t;            // the wave's 16-column tile (logical group)
+            for (int t = 0; t < TN; ++t) {
+                const int u = TN * wave + t;           // the wave's 16-column tile (logical group)
                 i16x4 v[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int r = 32 * kb + tr_row + 4 * h;
-                    const char* addr = st + r * kSkRowBytes + b_swz(u, r) * 32 + tr_colb;
+                    const char* addr = st + r * T::ROW_BYTES + b_swz(u, r) * 32 + tr_colb;
                     v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)addr);
                 }
                 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -178,19 +192,19 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
             for (int mt = 0; mt < MT; ++mt) {
                 const int row = 16 * mt + a_frow;
                 const int chunk = (4 * kb + fG) ^ (row & 7);
-                const bf16x8 ay = *reinterpret_cast<const bf16x8*>(st + kSkBBytes + row * 128 + chunk * 16);
+                const bf16x8 ay = *reinterpret_cast<const bf16x8*>(st + T::B_BYTES + row * 128 + chunk * 16);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) acc[t][mt] = mfma16(bx[t], ay, acc[t][mt]);
+                for (int t = 0; t < TN; ++t) acc[t][mt] = mfma16(bx[t], ay, acc[t][mt]);
             }
         }
     };
 
     // lane holds rows m = 16 mt + (lane & 15), columns 4 (lane >> 4) + 0..3 of each 16-column tile
     auto store_c = [&](int strip) {
-        const int n0 = strip * kSkinnyStrip;
+        const int n0 = strip * SW;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int n = n0 + 32 * wave + 16 * t + 4 * (lane >> 4);
+        for (int t = 0; t < TN; ++t) {
+            const int n = n0 + 16 * (TN * wave + t) + 4 * (lane >> 4);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int m = 16 * mt + (lane & 15);
@@ -205,7 +219,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     // workspace slot of workgroup w's piece of `strip`: 0 for the strip its range starts in, else 1
     const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.ws);
     auto slot_off = [&](int wg, int seg, int t, int mt) {
-        return (uint32_t)((((((wg * 2 + seg) * 4 + wave) * 2 + t) * MT + mt) * 64 + lane) * 16);
+        return (uint32_t)((((((wg * 2 + seg) * 4 + wave) * TN + t) * MT + mt) * 64 + lane) * 16);
     };
     // pieces of `strip` belong to logical workgroups wf .. wl (in K order)
     auto pieces_of = [&](int strip, int& wf, int& wl) {
@@ -218,7 +232,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     auto store_partial = [&](int strip) {  // device scope; not waited for here
         const int seg = (strip == first_strip) ? 0 : 1;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < TN; ++t)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 buf_store16_dev(ws, sel_off(16 * mt + part_row < p.M, slot_off(w, seg, t, mt)), f4_bits(acc[t][mt]));
@@ -243,20 +257,20 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
         // a piece's slot: pieces after the first start their range inside the strip (slot 0);
         // the first piece's range starts there too only if it starts at the strip's first unit
         const int seg_first = (range_begin(p.split, wf) == strip * p.ks) ? 0 : 1;
-        constexpr int PB = 16 / MT;
-        f32x4 sum[2][MT];
+        constexpr int PB = (32 / (TN * MT)) > 0 ? 32 / (TN * MT) : 1;
+        f32x4 sum[TN][MT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < TN; ++t)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) sum[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int b0 = wf; b0 <= wl; b0 += PB) {
-            f32x4 v[PB][2][MT];
+            f32x4 v[PB][TN][MT];
 #pragma unroll
             for (int q = 0; q < PB; ++q) {
                 const int wg = b0 + q;
                 const int sq = (wg == wf) ? seg_first : 0;
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < TN; ++t)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         const uint32_t off = sel_off(wg <= wl && 16 * mt + part_row < p.M, slot_off(wg, sq, t, mt));
@@ -267,12 +281,12 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
 #pragma unroll
             for (int q = 0; q < PB; ++q)
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < TN; ++t)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) sum[t][mt] += v[q][t][mt];
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < TN; ++t)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[t][mt] = sum[t][mt];
         store_c(strip);
@@ -321,7 +335,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
                 }
             }
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < TN; ++t)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{};
         }
@@ -333,34 +347,43 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     if (red1 >= 0) reduce(red1);
 }
 
-hipError_t configure_skinny_kernels() {
-    hipError_t e = hipSuccess;
-    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<1>::LDS_BYTES);
-    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<2>::LDS_BYTES);
-    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<3>::LDS_BYTES);
-    e = e != hipSuccess ? e : hipFuncSetAttribute((const void*)skinny_gemm_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<4>::LDS_BYTES);
-    return e;
+template <int MT, int SW>
+static hipError_t configure_one() {
+    return hipFuncSetAttribute((const void*)skinny_gemm_kernel<MT, SW>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<MT, SW>::LDS_BYTES);
 }
-
-int skinny_slot_floats(int mtiles) {
+hipError_t configure_skinny_kernels() {
+    const hipError_t es[] = {configure_one<1, 128>(), configure_one<2, 128>(), configure_one<3, 128>(),
+                             configure_one<4, 128>(), configure_one<1, 256>(), configure_one<2, 256>(),
+                             configure_one<3, 256>(), configure_one<4, 256>()};
+    for (hipError_t e : es)
+        if (e != hipSuccess) return e;
+    return hipSuccess;
+}
+template <int SW>
+static int slot_floats(int mtiles) {
     switch (mtiles) {
-        case 1: return SkinnyTraits<1>::SLOT_FLOATS;
-        case 2: return SkinnyTraits<2>::SLOT_FLOATS;
-        case 3: return SkinnyTraits<3>::SLOT_FLOATS;
-        default: return SkinnyTraits<4>::SLOT_FLOATS;
+        case 1: return SkinnyTraits<1, SW>::SLOT_FLOATS;
+        case 2: return SkinnyTraits<2, SW>::SLOT_FLOATS;
+        case 3: return SkinnyTraits<3, SW>::SLOT_FLOATS;
+        default: return SkinnyTraits<4, SW>::SLOT_FLOATS;
     }
 }
-
-hipError_t launch_skinny_gemm(int mtiles, const SkinnyArgs& a, hipStream_t s) {
+int skinny_slot_floats(int mtiles, int strip) { return strip == 256 ? slot_floats<256>(mtiles) : slot_floats<128>(mtiles); }
+template <int SW>
+static hipError_t launch_sw(int mtiles, const SkinnyArgs& a, hipStream_t s) {
     const int grid = a.grid;
     switch (mtiles) {
-        case 1: skinny_gemm_kernel<1><<<grid, 256, SkinnyTraits<1>::LDS_BYTES, s>>>(a); break;
-        case 2: skinny_gemm_kernel<2><<<grid, 256, SkinnyTraits<2>::LDS_BYTES, s>>>(a); break;
-        case 3: skinny_gemm_kernel<3><<<grid, 256, SkinnyTraits<3>::LDS_BYTES, s>>>(a); break;
-        case 4: skinny_gemm_kernel<4><<<grid, 256, SkinnyTraits<4>::LDS_BYTES, s>>>(a); break;
+        case 1: skinny_gemm_kernel<1, SW><<<grid, 256, SkinnyTraits<1, SW>::LDS_BYTES, s>>>(a); break;
+        case 2: skinny_gemm_kernel<2, SW><<<grid, 256, SkinnyTraits<2, SW>::LDS_BYTES, s>>>(a); break;
+        case 3: skinny_gemm_kernel<3, SW><<<grid, 256, SkinnyTraits<3, SW>::LDS_BYTES, s>>>(a); break;
+        case 4: skinny_gemm_kernel<4, SW><<<grid, 256, SkinnyTraits<4, SW>::LDS_BYTES, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+hipError_t launch_skinny_gemm(int mtiles, int strip, const SkinnyArgs& a, hipStream_t s) {
+    return strip == 256 ? launch_sw<256>(mtiles, a, s) : launch_sw<128>(mtiles, a, s);
 }
 
 }  // namespace glk

@@ -57,7 +57,7 @@ struct SkinnyArgs {
     uint16_t* C;
     int M, N, K;
     int lda, ldb, ldc;
-    int strips;          // column strips of B (kSkinnyStrip columns each)
+    int strips;          // column strips of B (the launch's strip width, 128 or 256 columns, each)
     int ks;              // 64-row stages per strip, ceil(K / 64)
     int grid;            // workgroups; logical workgroup w takes range w of `split`
     UnitSplit split;     // grid balanced ranges of the strip-major list of U = strips * ks
@@ -67,11 +67,12 @@ struct SkinnyArgs {
     float* ws;           // 2 * grid * skinny_slot_floats(mtiles) floats
     uint32_t* counters;  // one per strip, zero between launches
 };
-constexpr int kSkinnyStrip = 128;   // columns per workgroup
+constexpr int kSkinnyStripMin = 128;  // narrowest strip (columns)
 constexpr int kSkinnyStage = 64;    // k rows per streamed unit
-hipError_t launch_skinny_gemm(int mtiles, const SkinnyArgs& a, hipStream_t s);
+// strip: 128 or 256 columns
+hipError_t launch_skinny_gemm(int mtiles, int strip, const SkinnyArgs& a, hipStream_t s);
 hipError_t configure_skinny_kernels();
-int skinny_slot_floats(int mtiles);  // workspace floats per (strip, K slice)
+int skinny_slot_floats(int mtiles, int strip);  // workspace floats per piece
 
 // ---- misc ------------------------------------------------------------------------------------
 hipError_t launch_zero_c(uint16_t* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);

@@ -49,18 +49,38 @@ static void finish_waves(Plan& p) { wave_efficiency(p.grid, p.slots, &p.wave_eff
 // The split of the strip-major list of (strip, stage) units into `grid` balanced ranges puts
 // every range boundary on a strip boundary whenever grid = strips * S: each workgroup then holds
 // one piece of one strip, and a strip has exactly S pieces (S = 1: no partials at all), so no
-// piece ends mid-range and the fixup is as short as it gets. The planner takes such an aligned
-// grid, with the most pieces per strip that fit one wave of workgroups, when it occupies enough
-// of the CUs: two thirds for up to two 16-row tiles of M, all but a sixteenth above that (wider
-// M does more work per byte and wants every CU). Otherwise Stream-K ranges over one workgroup per
-// CU cut the strips wherever they fall.
-static int64_t skinny_grid(int strips, int ks, int mtiles, int cus) {
-    const int64_t units = (int64_t)strips * ks;
-    const int64_t s = std::min<int64_t>(cus / strips, ks);
-    const int64_t aligned = (int64_t)strips * s;
-    const bool enough = (mtiles <= 2) ? 3 * aligned >= 2 * (int64_t)cus : 16 * aligned >= 15 * (int64_t)cus;
-    if (s >= 1 && enough) return aligned;
-    return std::min<int64_t>(units, cus);
+// piece ends mid-range and the fixup is as short as it gets. For each strip width the aligned
+// grid takes the most pieces per strip that fit one wave of workgroups; it counts when it
+// occupies enough of the CUs: two thirds for up to two 16-row tiles of M, all but a sixteenth
+// above that (wider M does more work per byte and wants every CU). The planner takes the largest
+// counting grid, and on a tie the one with fewer pieces per strip (less float32 partial traffic).
+// 256-column strips are considered only up to two tiles of M: their stages are twice as big, and
+// with wider A the ring would be too shallow. Without an aligned grid, Stream-K ranges over one
+// workgroup per CU cut 128-column strips wherever they fall.
+static void skinny_layout(int64_t N, int ks, int mtiles, int cus, int* strip, int64_t* grid) {
+    int best_sw = 0;
+    int64_t best_grid = 0, best_s = 0;
+    for (int sw : {128, 256}) {
+        if (sw == 256 && mtiles > 2) continue;
+        const int64_t strips = cdiv(N, sw);
+        const int64_t s = std::min<int64_t>(cus / strips, ks);
+        if (s < 1) continue;
+        const int64_t g = strips * s;
+        const bool enough = (mtiles <= 2) ? 3 * g >= 2 * (int64_t)cus : 16 * g >= 15 * (int64_t)cus;
+        if (!enough) continue;
+        if (g > best_grid || (g == best_grid && s < best_s)) {
+            best_sw = sw;
+            best_grid = g;
+            best_s = s;
+        }
+    }
+    if (best_sw) {
+        *strip = best_sw;
+        *grid = best_grid;
+    } else {
+        *strip = kSkinnyStripMin;
+        *grid = std::min<int64_t>(cdiv(N, kSkinnyStripMin) * ks, cus);
+    }
 }
 
 static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
@@ -69,13 +89,13 @@ static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) 
     p.nxcd = dev.nxcd;
     p.mtiles = (int)cdiv(M, 16);
     p.threads = 256;
-    p.strips = (int)cdiv(N, kSkinnyStrip);
     p.ks = (int)cdiv(K, kSkinnyStage);
-    const int64_t units = (int64_t)p.strips * p.ks;
-    // one workgroup per CU at most (the LDS ring takes ~128 KB)
+    // one workgroup per CU at most (the LDS ring takes 128 KB or more)
     p.slots = dev.cus;
-    p.grid = skinny_grid(p.strips, p.ks, p.mtiles, dev.cus);
-    const int64_t slot_floats = skinny_slot_floats(p.mtiles);
+    skinny_layout(N, p.ks, p.mtiles, dev.cus, &p.strip, &p.grid);
+    p.strips = (int)cdiv(N, p.strip);
+    const int64_t units = (int64_t)p.strips * p.ks;
+    const int64_t slot_floats = skinny_slot_floats(p.mtiles, p.strip);
     // two partial slots per workgroup; fall back to one unit range per strip (no partials) if
     // the workspace or the counters cannot hold them
     if (2 * p.grid * slot_floats > dev.ws_floats || p.strips > dev.ws_counters) p.grid = p.strips;
@@ -86,7 +106,7 @@ static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) 
     p.reason = "M <= 64: weights streamed once, " + std::to_string(p.grid) +
                ((p.grid % p.strips == 0) ? " workgroups, each one piece of one strip, over "
                                          : " workgroups over ") +
-               std::to_string(units) + " strip stages";
+               std::to_string(units) + " stages of " + std::to_string(p.strip) + "-column strips";
     return p;
 }
 
@@ -175,7 +195,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast
         return p;
     }
     // the skinny kernel counts its (strip, stage) units in 32 bits
-    const bool units_fit = cdiv(N, kSkinnyStrip) * cdiv(K, kSkinnyStage) <= INT32_MAX;
+    const bool units_fit = cdiv(N, kSkinnyStripMin) * cdiv(K, kSkinnyStage) <= INT32_MAX;
     const bool skinny = units_fit && ((force == 1) || (force == 0 && M <= 64));
     return skinny ? plan_skinny(M, N, K, dev) : plan_tile(M, N, K, dev);
 }
@@ -197,14 +217,14 @@ std::string plan_json(const Plan& p, int64_t M, int64_t N, int64_t K) {
              "{\"M\": %lld, \"N\": %lld, \"K\": %lld, \"kernel\": \"%s\", \"bm\": %d, \"bn\": %d, "
              "\"bk\": %d, \"threads\": %d, \"tiles_m\": %lld, \"tiles_n\": %lld, \"tiles\": %lld, "
              "\"schedule\": \"%s\", \"splits\": %d, \"kt_per_split\": %d, \"group_m\": %d, "
-             "\"nxcd\": %d, \"mtiles\": %d, \"strips\": %d, \"ks\": %d, \"grid\": %lld, "
+             "\"nxcd\": %d, \"mtiles\": %d, \"strip\": %d, \"strips\": %d, \"ks\": %d, \"grid\": %lld, "
              "\"slots\": %lld, \"waves\": %lld, \"wave_eff\": %.6f, \"ws_floats\": %lld, "
              "\"reason\": \"%s\"}",
              (long long)M, (long long)N, (long long)K, kernel_name(p.kernel), p.bm, p.bn, p.bk,
              p.threads, (long long)p.tiles_m, (long long)p.tiles_n, (long long)p.tiles,
              p.kernel == kKernTile ? (p.sched == kSchedSplitK ? "split-k" : "data-parallel")
                                    : (p.kernel == kKernSkinny ? "strips" : "-"),
-             p.splits, p.kt_per_split, p.group_m, p.nxcd, p.mtiles, p.strips, p.ks,
+             p.splits, p.kt_per_split, p.group_m, p.nxcd, p.mtiles, p.strip, p.strips, p.ks,
              (long long)p.grid, (long long)p.slots, (long long)p.waves, p.wave_eff,
              (long long)p.ws_floats, p.reason.c_str());
     return std::string(buf);

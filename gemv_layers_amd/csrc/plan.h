@@ -24,7 +24,8 @@ struct Plan {
     int nxcd = 1;
     // skinny kernel
     int mtiles = 0;          // 16-row tiles of M
-    int strips = 0;          // 128-column strips
+    int strip = 128;         // skinny strip width: 128 or 256 columns
+    int strips = 0;          // column strips
     int ks = 0;              // 64-row stages per strip (skinny: units = strips * ks)
     // launch
     int64_t grid = 0;

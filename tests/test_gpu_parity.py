@@ -105,11 +105,13 @@ def test_skinny_kernel_float_and_exact(M, N, K):
     check_exact(run("skinny", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"skinny int {M}x{N}x{K}")
 
 
-# Stream-K ranges of the skinny kernel that cross strip boundaries: with 129..170 strips (or, for
-# three or more 16-row tiles of M, any count whose aligned grid leaves a sixteenth of the CUs
-# idle) 256 ranges cut the strips wherever they fall. A range may end inside a strip (announced at the range's end)
-# or contain a strip's end (announced mid-stream); ragged N and K included.
-STREAMK_SHAPES = [(3, 128 * 141 + 8, 64 * 37 + 8), (1, 128 * 150, 64 * 40), (2, 128 * 135 + 24, 64 * 33 + 24),
+# Stream-K ranges of the skinny kernel that cross strip boundaries: with too few strips of
+# either width for an aligned grid to fill two thirds of the CUs (more than 256 strips of 128
+# columns and 129..170 of 256), or, for three or more 16-row tiles of M, an aligned grid that
+# leaves a sixteenth of the CUs idle, 256 ranges cut the strips wherever they fall. A range may end
+# inside a strip (announced at the range's end) or contain a strip's end (announced mid-stream);
+# ragged N and K included.
+STREAMK_SHAPES = [(3, 256 * 150 + 8, 64 * 17 + 8), (1, 256 * 140, 64 * 20), (2, 256 * 135 + 24, 64 * 15 + 24),
                   (33, 128 * 131, 2056), (64, 128 * 145, 64 * 16)]
 
 
@@ -129,9 +131,9 @@ def test_skinny_stream_k_boundaries(M, N, K):
     check_exact(run("skinny", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"skinny int {M}x{N}x{K}")
 
 
-# Aligned layouts (grid = strips x pieces, every range one piece of one strip): few pieces on
-# two thirds of the CUs, and strips cut into many pieces (long fixups in batches), for one to four
-# 16-row tiles of M.
+# Aligned layouts (grid = strips x pieces, every range one piece of one strip), with 128- and
+# 256-column strips: few pieces on two thirds of the CUs, and strips cut into many pieces (long
+# fixups in batches), for one to four 16-row tiles of M.
 ALIGNED_SHAPES = [(1, 128 * 65, 4096), (5, 128 * 65 + 8, 1000), (64, 128 * 9, 64 * 300), (1, 128 * 7, 64 * 400),
                   (17, 128 * 7 + 40, 64 * 300 + 8), (40, 128 * 11, 12872)]
 

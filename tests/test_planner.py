@@ -88,7 +88,7 @@ def test_decode_shapes_stream_weights(name):
     p = g.gemm_plan_describe(w.M, w.N, w.K, 256)
     assert p["kernel"] == "skinny"
     assert p["mtiles"] == _cdiv(w.M, 16)
-    assert p["strips"] == _cdiv(w.N, 128)
+    assert p["strip"] in (128, 256) and p["strips"] == _cdiv(w.N, p["strip"])
     assert p["ks"] == _cdiv(w.K, 64)
     # at most one workgroup per CU: either every range is one piece of one strip on at least two
     # thirds of the CUs, or Stream-K ranges over all of them
@@ -96,21 +96,23 @@ def test_decode_shapes_stream_weights(name):
     assert (p["grid"] % p["strips"] == 0 and 3 * p["grid"] >= 2 * 256) or p["grid"] == 256
 
 
-# (M, N, K) -> grid: an aligned grid (strips x the most pieces per strip that fit 256) when it
-# fills two thirds of the CUs (one or two 16-row tiles of M) or fifteen sixteenths (more rows);
-# else Stream-K ranges over min(units, 256) workgroups
-LAYOUTS = [((1, 4096, 11008), 256),       # 32 strips x 8 pieces
-           ((1, 11008, 4096), 172),       # 86 strips x 2 pieces: two thirds of the CUs
-           ((64, 11008, 4096), 256),      # the same 172 is too few for four tiles of M: Stream-K
-           ((1, 128 * 65, 4096), 195),    # 65 x 3
-           ((1, 18056, 4096), 256),       # 142 strips, 142 < 171: Stream-K
-           ((3, 256, 128), 4),            # 2 strips x 2 stages: one unit per workgroup
-           ((1, 4096, 64), 32)]           # one stage per strip
+# (M, N, K) -> (strip width, grid): the largest aligned grid (strips x the most pieces per strip
+# that fit 256) that fills two thirds of the CUs (one or two 16-row tiles of M; 256-column strips
+# only there) or fifteen sixteenths (more rows), ties to fewer pieces per strip; else Stream-K
+# ranges over min(units, 256) workgroups with 128-column strips
+LAYOUTS = [((1, 4096, 11008), (128, 256)),      # 32 x 8 ties 16 x 16 at 256: fewer pieces
+           ((1, 11008, 4096), (256, 215)),      # 43 x 5 beats 86 x 2 = 172
+           ((64, 11008, 4096), (128, 256)),     # 86 x 2 is too few for four tiles of M: Stream-K
+           ((1, 128 * 65, 4096), (256, 231)),   # 33 x 7 beats 65 x 3 = 195
+           ((1, 256 * 140, 4096), (128, 256)),  # 280 strips of 128, 140 of 256: Stream-K
+           ((3, 256, 128), (128, 4)),           # 2 strips x 2 stages: one unit per workgroup
+           ((1, 4096, 64), (128, 32))]          # one stage per strip
 
 
 @pytest.mark.parametrize("shape,want", LAYOUTS)
 def test_skinny_layout_choice(shape, want):
-    assert g.gemm_plan_describe(*shape, 256)["grid"] == want
+    p = g.gemm_plan_describe(*shape, 256)
+    assert (p["strip"], p["grid"]) == want
 
 
 def test_skinny_small_problem_has_one_unit_per_workgroup():
