@@ -370,6 +370,26 @@ def main():
             torch.cuda.synchronize()
             graph_us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
             del graph
+            # a lone call replayed from a one-call graph, timed like the lone launch above
+            lone = []
+            for i in range(copies):
+                gi = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gi):
+                    g.gemm_bf16(wd.M, wd.N, wd.K, P(Ad), wd.K, P(Bs[i]), wd.N, P(Cd), wd.N,
+                                g.current_stream_handle())
+                lone.append(gi)
+            for gi in lone:
+                gi.replay()
+            torch.cuda.synchronize()
+            graph_singles = []
+            for i in range(48):
+                e0, e1 = events(2)
+                e0.record(stream)
+                lone[i % copies].replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                graph_singles.append(e0.elapsed_time(e1) * 1e3)
+            del lone
             single_us = float(np.median(singles))
             rec = {"us_single_median": round(single_us, 2),
                    "us_single_min": round(float(np.min(singles)), 2),
@@ -377,6 +397,7 @@ def main():
                    "gbps_single": round(wd.bytes / (single_us * 1e-6) / 1e9, 1),
                    "gbps_back_to_back": round(wd.bytes / (b2b_us * 1e-6) / 1e9, 1),
                    "us_graph_replay": round(graph_us, 2),
+                   "us_graph_single_median": round(float(np.median(graph_singles)), 2),
                    "gbps_graph_replay": round(wd.bytes / (graph_us * 1e-6) / 1e9, 1),
                    "plan_splits": g.gemm_last_plan().get("splits")}
             if "hbm_copy_gbps" in peaks:

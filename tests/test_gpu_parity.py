@@ -328,6 +328,42 @@ GRAPH_CASES = [("auto", 1, 4096, 11008), ("skinny", 3, 128 * 141 + 8, 64 * 37 + 
                ("auto", 64, 11008, 4096), ("tiled", 1000, 1000, 1000)]
 
 
+class _KernelNodeParams(ctypes.Structure):  # hipKernelNodeParams
+    _fields_ = [("blockDim", ctypes.c_uint * 3), ("extra", ctypes.c_void_p), ("func", ctypes.c_void_p),
+                ("gridDim", ctypes.c_uint * 3), ("kernelParams", ctypes.c_void_p),
+                ("sharedMemBytes", ctypes.c_uint)]
+
+
+def graph_nodes(graph):
+    """(node type, kernel name or None) for every node of a captured, kept graph.
+
+    Uses the HIP runtime the process already has mapped (torch's), so the graph handle is valid
+    for it. Node type 0 is a kernel node, 2 a memset node.
+    """
+    paths = sorted({ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln})
+    assert len(paths) == 1, f"expected one HIP runtime in the process, found {paths}"
+    hip = ctypes.CDLL(paths[0])
+    hip.hipKernelNameRefByPtr.restype = ctypes.c_char_p
+    hip.hipKernelNameRefByPtr.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    handle = ctypes.c_void_p(graph.raw_cuda_graph())
+    count = ctypes.c_size_t(0)
+    assert hip.hipGraphGetNodes(handle, None, ctypes.byref(count)) == 0
+    nodes = (ctypes.c_void_p * max(count.value, 1))()
+    assert hip.hipGraphGetNodes(handle, nodes, ctypes.byref(count)) == 0
+    out = []
+    for i in range(count.value):
+        kind = ctypes.c_int(-1)
+        assert hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(kind)) == 0
+        name = None
+        if kind.value == 0:
+            prm = _KernelNodeParams()
+            assert hip.hipGraphKernelNodeGetParams(ctypes.c_void_p(nodes[i]), ctypes.byref(prm)) == 0
+            raw = hip.hipKernelNameRefByPtr(prm.func, None)
+            name = raw.decode() if raw else ""
+        out.append((kind.value, name))
+    return out
+
+
 @pytest.mark.parametrize("entry,M,N,K", GRAPH_CASES)
 def test_graph_replay_matches_eager(entry, M, N, K):
     A = matrix("normal", M, K, seed=9100 + M)
@@ -347,10 +383,20 @@ def test_graph_replay_matches_eager(entry, M, N, K):
                        ctypes.c_void_p(C.data_ptr()), N, g.current_stream_handle())
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
+    g.gemm_fill_launch(ctypes.c_void_p(C.data_ptr()), C.numel() * 2, POISON)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph(keep_graph=True)
     with torch.cuda.graph(graph):
         ENTRIES[entry](M, N, K, ctypes.c_void_p(dA.data_ptr()), K, ctypes.c_void_p(dB.data_ptr()), N,
                        ctypes.c_void_p(C.data_ptr()), N, g.current_stream_handle())
+    torch.cuda.synchronize()
+    # the capture recorded the product as one kernel node (and no memset node), and ran nothing
+    nodes = graph_nodes(graph)
+    family = "skinny_gemm_kernel" if entry == "skinny" or (entry == "auto" and M <= 64) else "tile_gemm_kernel"
+    assert len(nodes) == 1 and nodes[0][0] == 0, f"{entry} {M}x{N}x{K}: captured nodes {nodes}"
+    assert family in nodes[0][1], f"{entry} {M}x{N}x{K}: captured kernel {nodes[0][1]}"
+    assert np.all(host(C) == np.uint16(POISON & 0xFFFF)), "capture wrote C"
+    graph.instantiate()
     for rep in range(4):
         g.gemm_fill_launch(ctypes.c_void_p(C.data_ptr()), C.numel() * 2, POISON)
         (m, n, k), a, b, c = other[rep % 2], oA[rep % 2], oB[rep % 2], oC[rep % 2]
