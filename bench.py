@@ -74,6 +74,11 @@ def parse():
     ap.add_argument("--large", action="store_true", help="also time sq8192, sq16384, mlp_up/down")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-torch", action="store_true", help="skip the torch.matmul comparison")
+    ap.add_argument("--no-swiglu", action="store_true",
+                    help="skip the fused gate/up SwiGLU workloads")
+    ap.add_argument("--swiglu-unfused-ours", action="store_true",
+                    help="also time the unfused SwiGLU path on this library's own product (it runs "
+                         "the plain kernels, which then also appear in a profile of this command)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run the copy kernel 3 times over 256 MiB (known traffic) so that a "
                          "counter pass over this command also calibrates FETCH_SIZE / WRITE_SIZE")
@@ -406,6 +411,88 @@ def main():
             del Ad, Cd
         del shapes
         out["decode"] = dec
+
+    # ---------------- fused gate/up SwiGLU ----------------
+    # silu(A Wg) * (A Wu) in one call on the K x 2N gate/up weight, against the same work in
+    # PyTorch (torch.matmul into an M x 2N bf16 intermediate, then silu and multiply) and, with
+    # --swiglu-unfused-ours, against this library's own product followed by the same two ops
+    if not args.no_swiglu:
+        import torch.nn.functional as F
+
+        glu = {}
+        mfma_peak = 2500.0
+        for name in ("glu_prefill", "glu_dec_M1", "glu_dec_M16", "glu_dec_M64"):
+            wg = WORKLOADS[name]
+            log(f"swiglu {name}")
+            M, N, K = wg.M, wg.N, wg.K
+            copies = 1 if wg.bound == "mfma" else 12  # decode: cold weights, rotated
+            b0 = dev(matrix("normal", K, 2 * N, seed=wg.seed_b, sigma=wg.sigma_b))
+            Bs = [b0] + [b0.clone() for _ in range(copies - 1)]
+            Ag = dev(matrix("normal", M, K, seed=wg.seed_a, sigma=wg.sigma_a))
+            Hg = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            Gu = torch.empty((M, 2 * N), dtype=torch.bfloat16, device="cuda")
+            Hu = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+            def fused(b):
+                g.gemm_bf16_swiglu(M, N, K, P(Ag), K, P(b), 2 * N, P(Hg), N, sh)
+
+            def unfused_ours(b):
+                g.gemm_bf16(M, 2 * N, K, P(Ag), K, P(b), 2 * N, P(Gu), 2 * N, sh)
+                torch.mul(F.silu(Gu[:, :N]), Gu[:, N:], out=Hu)
+
+            def unfused_torch(b):
+                torch.matmul(Ag, b, out=Gu)
+                torch.mul(F.silu(Gu[:, :N]), Gu[:, N:], out=Hu)
+
+            def per_call_us(fn, n, rounds=3):
+                """Mean per call of n calls back to back between two events, per round."""
+                for i in range(2 * copies):
+                    fn(Bs[i % copies])
+                torch.cuda.synchronize()
+                res = []
+                for _ in range(rounds):
+                    e0, e1 = events(2)
+                    e0.record(stream)
+                    for i in range(n):
+                        fn(Bs[i % copies])
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    res.append(e0.elapsed_time(e1) * 1e3 / n)
+                return np.array(res)
+
+            n = 10 if wg.bound == "mfma" else 96
+            t_f = per_call_us(fused, n)
+            plan = g.gemm_last_plan()
+            mean_f = float(t_f.mean())
+            rec = {"M": M, "N": N, "K": K, "us_mean": round(mean_f, 2),
+                   "us_best_round": round(float(t_f.min()), 2),
+                   "kernel": plan.get("kernel"), "strip": plan.get("strip"),
+                   "grid": plan.get("grid")}
+            if not args.no_torch:
+                mean_t = float(per_call_us(unfused_torch, n).mean())
+                rec["torch_unfused_us_mean"] = round(mean_t, 2)
+                rec["speedup_vs_torch_unfused"] = round(mean_t / mean_f, 3)
+            if args.swiglu_unfused_ours:
+                mean_u = float(per_call_us(unfused_ours, n).mean())
+                rec["unfused_ours_us_mean"] = round(mean_u, 2)
+                rec["speedup_vs_unfused_ours"] = round(mean_u / mean_f, 3)
+            if wg.bound == "mfma":
+                tf = wg.flops / (mean_f * 1e-6) / 1e12
+                rec.update({"tflops": round(tf, 1),
+                            "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                         "peak": mfma_peak, "unit": "TFLOP/s",
+                                         "frac": round(tf / mfma_peak, 4)}})
+            else:
+                gb = wg.bytes / (mean_f * 1e-6) / 1e9
+                rec.update({"gbps": round(gb, 1),
+                            "roofline": {"bound": "hbm", "achieved": round(gb, 1),
+                                         "peak": 8000.0, "unit": "GB/s",
+                                         "frac": round(gb / 8000.0, 4)}})
+                if "hbm_copy_gbps" in peaks:
+                    rec["frac_of_measured_copy"] = round(gb / peaks["hbm_copy_gbps"], 4)
+            glu[name] = rec
+            del Bs, b0, Ag, Hg, Gu, Hu
+        out["swiglu"] = glu
 
     # ---------------- more compute-bound workloads ----------------
     if args.large:

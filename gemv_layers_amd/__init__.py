@@ -23,9 +23,13 @@ GEMM_ERR_UNSUPPORTED = 2
 GEMM_ERR_NOT_INITIALIZED = 3
 GEMM_ERR_HIP = 4
 
+GEMM_PLAN_SKINNY = 1
+GEMM_PLAN_SWIGLU = 2
+
 # every symbol include/gemm_bf16.h declares
 EXPORTS = (
-    "gemm_init", "gemm_bf16", "gemm_bf16_skinny", "gemm_bf16_tiled", "gemm_plan_describe",
+    "gemm_init", "gemm_bf16", "gemm_bf16_skinny", "gemm_bf16_tiled", "gemm_bf16_swiglu",
+    "gemm_plan_describe",
     "gemm_wave_efficiency", "gemm_last_plan", "gemm_status_string", "gemm_finalize",
     "gemm_peak_mfma_launch", "gemm_peak_copy_launch", "gemm_peak_read_launch",
     "gemm_peak_clock_launch",
@@ -53,7 +57,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     i64, i32, p, u32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint32
     gemm_sig = [i64, i64, i64, p, i64, p, i64, p, i64, p]
-    for name in ("gemm_bf16", "gemm_bf16_skinny", "gemm_bf16_tiled"):
+    for name in ("gemm_bf16", "gemm_bf16_skinny", "gemm_bf16_tiled", "gemm_bf16_swiglu"):
         getattr(L, name).argtypes = gemm_sig
         getattr(L, name).restype = i32
     L.gemm_init.argtypes = [i32]
@@ -123,9 +127,16 @@ def gemm_bf16_tiled(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
     _call("gemm_bf16_tiled", M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
-def gemm_plan_describe(M: int, N: int, K: int, cus: int = 256, skinny: bool = False) -> dict:
+def gemm_bf16_swiglu(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
+    """C = silu(A * B[:, :N]) * (A * B[:, N:2N]) on raw device pointers; B is K x 2N."""
+    _call("gemm_bf16_swiglu", M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_plan_describe(M: int, N: int, K: int, cus: int = 256, skinny: bool = False,
+                       swiglu: bool = False) -> dict:
     buf = ctypes.create_string_buffer(4096)
-    _check("gemm_plan_describe", lib().gemm_plan_describe(M, N, K, cus, int(skinny), buf, 4096))
+    flags = (GEMM_PLAN_SKINNY if skinny else 0) | (GEMM_PLAN_SWIGLU if swiglu else 0)
+    _check("gemm_plan_describe", lib().gemm_plan_describe(M, N, K, cus, flags, buf, 4096))
     return json.loads(buf.value.decode())
 
 
@@ -197,5 +208,30 @@ def matmul(A, B, out=None, entry: str = "auto", stream=None):
     st = stream if stream is not None else current_stream_handle()
     _call(_ENTRY[entry], M, N, K, ctypes.c_void_p(A.data_ptr()), max(A.stride(0), K),
           ctypes.c_void_p(B.data_ptr()), max(B.stride(0), N), ctypes.c_void_p(out.data_ptr()),
+          max(out.stride(0), N), st)
+    return out
+
+
+def swiglu_matmul(A, B, out=None, stream=None):
+    """silu(A @ B[:, :N]) * (A @ B[:, N:]) for bf16 CUDA tensors, B of shape (K, 2N): the gate
+    and up weights side by side. Returns the (M, N) bf16 result."""
+    import torch
+
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0] or B.shape[1] % 2:
+        raise ValueError("B must be K x 2N for A of shape M x K")
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("A and B must be device tensors")
+    M, K = A.shape
+    N = B.shape[1] // 2
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    for t in (A, B, out):
+        if t.numel() and t.stride(1) != 1:
+            raise ValueError("unit column stride required")
+    st = stream if stream is not None else current_stream_handle()
+    _call("gemm_bf16_swiglu", M, N, K, ctypes.c_void_p(A.data_ptr()), max(A.stride(0), K),
+          ctypes.c_void_p(B.data_ptr()), max(B.stride(0), 2 * N), ctypes.c_void_p(out.data_ptr()),
           max(out.stride(0), N), st)
     return out

@@ -2,6 +2,7 @@
 // any HIP call, per-device state and workspace, planning and dispatch onto the caller's stream.
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -44,21 +45,23 @@ int copy_out(const std::string& s, char* buf, int len) {
     return GEMM_OK;
 }
 
+// glu: B holds 2N columns (gate, then up)
 int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-             int64_t ldb, const void* C, int64_t ldc) {
+             int64_t ldb, const void* C, int64_t ldc, bool glu) {
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+    if (glu && N > INT64_MAX / 2) return GEMM_ERR_INVALID_ARG;
     if (ldc < N || ldc < 0) return GEMM_ERR_INVALID_ARG;
-    if (lda < K || ldb < N) return GEMM_ERR_INVALID_ARG;
+    if (lda < K || ldb < (glu ? 2 * N : N)) return GEMM_ERR_INVALID_ARG;
     if (M > 0 && N > 0 && C == nullptr) return GEMM_ERR_INVALID_ARG;
     if (M > 0 && K > 0 && A == nullptr) return GEMM_ERR_INVALID_ARG;
     if (K > 0 && N > 0 && B == nullptr) return GEMM_ERR_INVALID_ARG;
     return GEMM_OK;
 }
 
-// force: 0 dispatch on M, 1 skinny, 2 large-tile family
+// force: 0 dispatch on M, 1 skinny, 2 large-tile family; glu: the SwiGLU form
 int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-        void* C, int64_t ldc, hipStream_t stream, int force) {
-    int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+        void* C, int64_t ldc, hipStream_t stream, int force, bool glu = false) {
+    int st = validate(M, N, K, A, lda, B, ldb, C, ldc, glu);
     if (st != GEMM_OK) return st;
     if (force == 1 && (M < 1 || M > 64)) return GEMM_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return GEMM_OK;
@@ -68,8 +71,10 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
     DeviceState& ds = g_dev[dev];
     if (!ds.ready) return GEMM_ERR_NOT_INITIALIZED;
 
-    const bool fast = glk::fast_path_ok(M, N, K, A, lda, B, ldb, C, ldc);
-    const glk::Plan p = glk::make_plan(M, N, K, ds.info, fast, force);
+    // (the SwiGLU form's up half starts N columns in: N % 8 == 0 keeps it 16-byte aligned)
+    const bool fast = glk::fast_path_ok(M, glu ? 2 * N : N, K, A, lda, B, ldb, C, ldc) &&
+                      glk::fast_path_ok(M, N, K, A, lda, B, ldb, C, ldc);
+    const glk::Plan p = glk::make_plan(M, N, K, ds.info, fast, force, glu);
     const uint16_t* a16 = static_cast<const uint16_t*>(A);
     const uint16_t* b16 = static_cast<const uint16_t*>(B);
     uint16_t* c16 = static_cast<uint16_t*>(C);
@@ -81,7 +86,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
             e = glk::launch_zero_c(c16, M, N, ldc, stream);
             break;
         case glk::kKernGeneric:
-            e = glk::launch_generic_gemm(a16, b16, c16, M, N, K, lda, ldb, ldc, stream);
+            e = glk::launch_generic_gemm(a16, b16, c16, M, N, K, lda, ldb, ldc, glu, stream);
             break;
         case glk::kKernTile: {
             glk::TileArgs t;
@@ -103,7 +108,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
             t.kt_per_split = p.kt_per_split;
             t.ws = ds.ws;
             t.counters = ds.counters;
-            e = glk::launch_tile_gemm(p.tile_cfg, t, (int)p.grid, stream);
+            e = glk::launch_tile_gemm(p.tile_cfg, t, (int)p.grid, glu, stream);
             break;
         }
         case glk::kKernSkinny: {
@@ -124,7 +129,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
             s.nxcd = p.nxcd;
             s.ws = ds.ws;
             s.counters = ds.counters;
-            e = glk::launch_skinny_gemm(p.mtiles, p.strip, s, stream);
+            e = glk::launch_skinny_gemm(p.mtiles, p.strip, glu, s, stream);
             break;
         }
         default:
@@ -199,15 +204,22 @@ int gemm_bf16_tiled(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
     return run(M, N, K, A, lda, B, ldb, C, ldc, reinterpret_cast<hipStream_t>(stream), 2);
 }
 
-int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int skinny, char* buf, int len) {
-    if (M < 0 || N < 0 || K < 0 || cus <= 0) return GEMM_ERR_INVALID_ARG;
+int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, void* C, int64_t ldc, gemm_stream_t stream) {
+    return run(M, N, K, A, lda, B, ldb, C, ldc, reinterpret_cast<hipStream_t>(stream), 0, true);
+}
+
+int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int flags, char* buf, int len) {
+    if (M < 0 || N < 0 || K < 0 || cus <= 0 || (flags & ~3)) return GEMM_ERR_INVALID_ARG;
+    const bool skinny = (flags & GEMM_PLAN_SKINNY) != 0, glu = (flags & GEMM_PLAN_SWIGLU) != 0;
+    if (glu && N > INT64_MAX / 2) return GEMM_ERR_INVALID_ARG;
     if (skinny && (M < 1 || M > 64)) return GEMM_ERR_UNSUPPORTED;
     glk::DeviceInfo dev;
     dev.cus = cus;
     dev.nxcd = (cus % 8 == 0) ? 8 : 1;
     dev.ws_floats = kWsFloats;
     dev.ws_counters = kWsCounters;
-    const glk::Plan p = glk::make_plan(M, N, K, dev, true, skinny ? 1 : 0);
+    const glk::Plan p = glk::make_plan(M, N, K, dev, true, skinny ? 1 : 0, glu);
     return copy_out(glk::plan_json(p, M, N, K), buf, len);
 }
 

@@ -138,6 +138,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
+// SwiGLU of one gate/up accumulator pair: silu(g) * u, silu(x) = x / (1 + e^-x), in float32 with
+// the library exponential and IEEE division. Large g gives g * u; below about -88 the exponential
+// overflows and the result is -0 * u, the float32 limit of the exact value.
+__device__ __forceinline__ float swiglu1(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+__device__ __forceinline__ f32x4 swiglu4(f32x4 g, f32x4 u) {
+    return f32x4{swiglu1(g[0], u[0]), swiglu1(g[1], u[1]), swiglu1(g[2], u[2]), swiglu1(g[3], u[3])};
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 

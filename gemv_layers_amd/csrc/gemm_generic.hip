@@ -2,6 +2,8 @@
 // dimensions or N, K not multiples of 8, extents beyond the fast kernels' 32-bit offsets).
 // Same contract: bf16 in, float32 accumulation, bf16 out (round to nearest even). Element-wise
 // bounds-checked loads through LDS; each thread accumulates a 4 x 4 block with float32 FMAs.
+// The SwiGLU form (GLU = true) keeps a second accumulator block for the up half of B (columns
+// N .. 2N-1) and writes silu(gate) * up.
 // Also the zero-fill for K == 0 and a plain 32-bit fill used to poison outputs and evict caches.
 
 #include "common.h"
@@ -13,6 +15,7 @@ __device__ __forceinline__ float load_bf16(const uint16_t* p) {
     return __builtin_bit_cast(float, (uint32_t)(*p) << 16);
 }
 
+template <bool GLU>
 __global__ void __launch_bounds__(256) generic_gemm_kernel(const uint16_t* __restrict__ A,
                                                            const uint16_t* __restrict__ B,
                                                            uint16_t* __restrict__ C, int64_t M,
@@ -21,10 +24,12 @@ __global__ void __launch_bounds__(256) generic_gemm_kernel(const uint16_t* __res
     constexpr int T = 64, KS = 16;
     __shared__ float sa[KS][T + 1];
     __shared__ float sb[KS][T + 1];
+    __shared__ float su[GLU ? KS : 1][T + 1];
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
     const int64_t m0 = (int64_t)blockIdx.y * T, n0 = (int64_t)blockIdx.x * T;
     float acc[4][4] = {};
+    float accu[4][4] = {};
     for (int64_t k0 = 0; k0 < K; k0 += KS) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -35,6 +40,7 @@ __global__ void __launch_bounds__(256) generic_gemm_kernel(const uint16_t* __res
             const int kb = e >> 6, nn = e & 63;
             const int64_t kr = k0 + kb, n = n0 + nn;
             sb[kb][nn] = (kr < K && n < N) ? load_bf16(B + kr * ldb + n) : 0.f;
+            if constexpr (GLU) su[kb][nn] = (kr < K && n < N) ? load_bf16(B + kr * ldb + N + n) : 0.f;
         }
         __syncthreads();
 #pragma unroll
@@ -48,6 +54,14 @@ __global__ void __launch_bounds__(256) generic_gemm_kernel(const uint16_t* __res
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+            if constexpr (GLU) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = su[kk][tx * 4 + j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) accu[i][j] = __builtin_fmaf(a[i], b[j], accu[i][j]);
+            }
         }
         __syncthreads();
     }
@@ -58,7 +72,8 @@ __global__ void __launch_bounds__(256) generic_gemm_kernel(const uint16_t* __res
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + tx * 4 + j;
-            if (n < N) C[m * ldc + n] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j]);
+            const float h = GLU ? swiglu1(acc[i][j], accu[i][j]) : acc[i][j];
+            if (n < N) C[m * ldc + n] = __builtin_bit_cast(uint16_t, (__bf16)h);
         }
     }
 }
@@ -83,10 +98,14 @@ __global__ void __launch_bounds__(256) fill_kernel(uint32_t* dst, int64_t words,
 
 hipError_t launch_generic_gemm(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M,
                                int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-                               hipStream_t s) {
+                               bool glu, hipStream_t s) {
     const int64_t gx = (N + 63) / 64, gy = (M + 63) / 64;
     if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
-    generic_gemm_kernel<<<dim3((unsigned)gx, (unsigned)gy), 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
+    const dim3 grid((unsigned)gx, (unsigned)gy);
+    if (glu)
+        generic_gemm_kernel<true><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
+    else
+        generic_gemm_kernel<false><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
     return hipGetLastError();
 }
 

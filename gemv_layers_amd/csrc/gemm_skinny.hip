@@ -33,6 +33,11 @@
 //   arriver loads every piece (all loads issued before any add), adds them in K order, writes
 //   bf16 and returns the counter to zero. Partials travel at device scope (written through to the
 //   device coherence point), whichever XCDs the pieces ran on.
+// * The SwiGLU form (GLU = true) computes h = silu(A Wg) * (A Wu), Wg and Wu the two halves of one
+//   K x 2N weight: a strip of SW columns in LDS covers SW / 2 outputs, each wave's first TN / 2
+//   tiles being gate columns and its last TN / 2 the same up columns (chosen per lane in the B
+//   loads), so the epilogue pairs tile t with tile t + TN / 2 in registers. Partials and their
+//   reduction are unchanged; the activation is applied where bf16 is written.
 
 #include "common.h"
 #include "kernels.h"
@@ -77,10 +82,12 @@ struct SkinnyTraits {
 // the groups 8 rows apart, land on different banks.
 __device__ __forceinline__ int b_swz(int u, int r) { return u ^ ((r & 3) | (((r >> 3) & 1) << 2)); }
 
-template <int MT, int SW>
+template <int MT, int SW, bool GLU>
 __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     using T = SkinnyTraits<MT, SW>;
     constexpr int TN = T::TN;
+    constexpr int SO = GLU ? SW / 2 : SW;    // output columns per strip
+    constexpr int TNO = GLU ? TN / 2 : TN;   // output tiles per wave
     constexpr int STAGES = T::STAGES;
     extern __shared__ __attribute__((aligned(1024))) char lds[];
 
@@ -98,15 +105,24 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     // byte 16 l of the instruction's 1 KB = row 4i + l/16 (of the wave's 16), physical 16-byte
     // chunk l%16, and fetches the logical chunk the swizzle keeps there (the swizzle is an
     // involution on the group index). Column validity is checked per unit (the strip varies).
+    // (SwiGLU: LDS column 16 u + c of tile t = u % TN of wave u / TN is output column
+    // 16 (TNO (u / TN) + t % TNO) + c of the strip, from the gate half for t < TNO, else the up
+    // half N columns further on)
     uint32_t b_off[T::B_PER_WAVE];
-    int b_col[T::B_PER_WAVE];
+    int b_col[T::B_PER_WAVE];  // output column within the strip, for the range check
 #pragma unroll
     for (int i = 0; i < T::B_PER_WAVE; ++i) {
         const int r = 16 * wave + T::ROWS_PER_INSTR * i + lane / T::CHUNKS;
         const int pc = lane % T::CHUNKS;
         const int u = b_swz(pc >> 1, r);
-        b_col[i] = 16 * u + 8 * (pc & 1);
-        b_off[i] = (uint32_t)(r * p.ldb + b_col[i]) * 2u;
+        if constexpr (GLU) {
+            const int t = u % TN;
+            b_col[i] = 16 * (TNO * (u / TN) + t % TNO) + 8 * (pc & 1);
+            b_off[i] = (uint32_t)(r * p.ldb + (t < TNO ? 0 : p.N) + b_col[i]) * 2u;
+        } else {
+            b_col[i] = 16 * u + 8 * (pc & 1);
+            b_off[i] = (uint32_t)(r * p.ldb + b_col[i]) * 2u;
+        }
     }
     // A: instruction j (= wave + 4t) covers A rows 8j .. 8j+7 of the padded M x 64 block;
     // lane l -> row 8j + l/8, physical chunk l%8 holding logical chunk (l%8) ^ (row & 7).
@@ -134,7 +150,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
             iss_stage = 0;
             ++iss_strip;
         }
-        const int n0 = strip * SW;
+        const int n0 = strip * SO;
         const int rows = (i < nunits) ? min(kSkRows, p.K - k0) : 0;  // uniform
         const i32x4 b_rsrc = rsrc_words(p.B + (size_t)k0 * p.ldb + n0, (uint32_t)rows * (uint32_t)p.ldb * 2u);
         const uint32_t st_lds = lds_addr(st);
@@ -200,16 +216,23 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     };
 
     // lane holds rows m = 16 mt + (lane & 15), columns 4 (lane >> 4) + 0..3 of each 16-column tile
+    // (SwiGLU: tile t holds the gate and tile t + TNO the up values of the same outputs)
     auto store_c = [&](int strip) {
-        const int n0 = strip * SW;
+        const int n0 = strip * SO;
 #pragma unroll
-        for (int t = 0; t < TN; ++t) {
-            const int n = n0 + 16 * (TN * wave + t) + 4 * (lane >> 4);
+        for (int t = 0; t < TNO; ++t) {
+            const int n = n0 + 16 * (TNO * wave + t) + 4 * (lane >> 4);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int m = 16 * mt + (lane & 15);
                 if (m < p.M && n < p.N) {
-                    u32x2 v = {pack_bf16x2(acc[t][mt][0], acc[t][mt][1]), pack_bf16x2(acc[t][mt][2], acc[t][mt][3])};
+                    f32x4 h;
+                    if constexpr (GLU) {
+                        h = swiglu4(acc[t][mt], acc[t + TNO][mt]);
+                    } else {
+                        h = acc[t][mt];
+                    }
+                    u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
                     *reinterpret_cast<u32x2*>(p.C + (size_t)m * p.ldc + n) = v;
                 }
             }
@@ -349,8 +372,12 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
 
 template <int MT, int SW>
 static hipError_t configure_one() {
-    return hipFuncSetAttribute((const void*)skinny_gemm_kernel<MT, SW>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<MT, SW>::LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)skinny_gemm_kernel<MT, SW, false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<MT, SW>::LDS_BYTES);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)skinny_gemm_kernel<MT, SW, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<MT, SW>::LDS_BYTES);
+    return e;
 }
 hipError_t configure_skinny_kernels() {
     const hipError_t es[] = {configure_one<1, 128>(), configure_one<2, 128>(), configure_one<3, 128>(),
@@ -370,20 +397,21 @@ static int slot_floats(int mtiles) {
     }
 }
 int skinny_slot_floats(int mtiles, int strip) { return strip == 256 ? slot_floats<256>(mtiles) : slot_floats<128>(mtiles); }
-template <int SW>
+template <int SW, bool GLU>
 static hipError_t launch_sw(int mtiles, const SkinnyArgs& a, hipStream_t s) {
     const int grid = a.grid;
     switch (mtiles) {
-        case 1: skinny_gemm_kernel<1, SW><<<grid, 256, SkinnyTraits<1, SW>::LDS_BYTES, s>>>(a); break;
-        case 2: skinny_gemm_kernel<2, SW><<<grid, 256, SkinnyTraits<2, SW>::LDS_BYTES, s>>>(a); break;
-        case 3: skinny_gemm_kernel<3, SW><<<grid, 256, SkinnyTraits<3, SW>::LDS_BYTES, s>>>(a); break;
-        case 4: skinny_gemm_kernel<4, SW><<<grid, 256, SkinnyTraits<4, SW>::LDS_BYTES, s>>>(a); break;
+        case 1: skinny_gemm_kernel<1, SW, GLU><<<grid, 256, SkinnyTraits<1, SW>::LDS_BYTES, s>>>(a); break;
+        case 2: skinny_gemm_kernel<2, SW, GLU><<<grid, 256, SkinnyTraits<2, SW>::LDS_BYTES, s>>>(a); break;
+        case 3: skinny_gemm_kernel<3, SW, GLU><<<grid, 256, SkinnyTraits<3, SW>::LDS_BYTES, s>>>(a); break;
+        case 4: skinny_gemm_kernel<4, SW, GLU><<<grid, 256, SkinnyTraits<4, SW>::LDS_BYTES, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
-hipError_t launch_skinny_gemm(int mtiles, int strip, const SkinnyArgs& a, hipStream_t s) {
-    return strip == 256 ? launch_sw<256>(mtiles, a, s) : launch_sw<128>(mtiles, a, s);
+hipError_t launch_skinny_gemm(int mtiles, int strip, bool glu, const SkinnyArgs& a, hipStream_t s) {
+    if (glu) return strip == 256 ? launch_sw<256, true>(mtiles, a, s) : launch_sw<128, true>(mtiles, a, s);
+    return strip == 256 ? launch_sw<256, false>(mtiles, a, s) : launch_sw<128, false>(mtiles, a, s);
 }
 
 }  // namespace glk

@@ -33,6 +33,12 @@
 // * Split pieces store float32 partials to a workspace slot with device-scope stores, then bump
 //   an arrival counter; the last arriver adds all pieces of the tile in K order, writes bf16 and
 //   returns the counter to zero for the next launch (no memset, no spin-waiting).
+// * The SwiGLU form (GLU = true) computes h = silu(A Wg) * (A Wu) with Wg and Wu the two halves
+//   of one K x 2N weight. A BN-wide tile then covers BN / 2 outputs: each wave's WTN columns in
+//   LDS are WTN / 2 gate columns followed by the same WTN / 2 up columns, chosen per lane in the
+//   B loads, so gate tile ni and up tile ni + TN / 2 of a lane hold the same outputs and the
+//   epilogue combines them in registers (spark-kernels post, "the memory-bound kernels": SwiGLU
+//   in one kernel instead of two, here fused into the product that makes its inputs).
 
 #include "common.h"
 #include "kernels.h"
@@ -91,11 +97,12 @@ __device__ __forceinline__ int a_swz(int c, int m) { return c ^ ((m >> 1) & 7); 
 // B: physical 32-byte column group of logical group u in k row k
 __device__ __forceinline__ int b_swz(int u, int k) { return u ^ (k & 7); }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool GLU>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
                                amdgpu_waves_per_eu(1, 1)))
 tile_gemm_kernel(TileArgs p) {
     using T = TileTraits<BM, BN, WM, WN>;
+    static_assert(!GLU || (T::TN % 2 == 0), "SwiGLU pairs gate and up tiles within a wave");
     constexpr int BK = T::BK, TM = T::TM, TN = T::TN;
     extern __shared__ __attribute__((aligned(1024))) char lds[];
 
@@ -120,7 +127,8 @@ tile_gemm_kernel(TileArgs p) {
     const int in_g = tile - g * per_group;
     const int tm = first_m + in_g % gm;
     const int tn = in_g / gm;
-    const int m0 = tm * BM, n0 = tn * BN;
+    // n0: first output column of the tile (a SwiGLU tile's BN columns make BN / 2 outputs)
+    const int m0 = tm * BM, n0 = tn * (GLU ? BN / 2 : BN);
     const int kt_total = (p.K + BK - 1) / BK;
     int kt_begin = 0, kt_end = kt_total;
     if (p.sched == kSchedSplitK) {
@@ -152,7 +160,14 @@ tile_gemm_kernel(TileArgs p) {
         const int k = (wave * T::B_PER_WAVE + i) * T::B_ROWS_PER_INSTR + lane / T::B_CHUNKS;
         const int pc = lane % T::B_CHUNKS;
         const int col = 16 * b_swz(pc >> 1, k) + 8 * (pc & 1);
-        b_off[i] = sel_off(n0 + col < p.N, (uint32_t)(k * p.ldb + col) * 2u);
+        if constexpr (GLU) {  // LDS column -> output column `out` of the gate or the up half
+            const int r = col % T::WTN;
+            const int out = (col / T::WTN) * (T::WTN / 2) + r % (T::WTN / 2);
+            const int src = (r < T::WTN / 2 ? 0 : p.N) + out;
+            b_off[i] = sel_off(n0 + out < p.N, (uint32_t)(k * p.ldb + src) * 2u);
+        } else {
+            b_off[i] = sel_off(n0 + col < p.N, (uint32_t)(k * p.ldb + col) * 2u);
+        }
     }
 
     // half h of A stage s (k 64 s .. 64 s + 63 of this workgroup's range) into A slot s % SA
@@ -313,16 +328,25 @@ tile_gemm_kernel(TileArgs p) {
     }
 
     // ---- epilogue: bf16 (round to nearest even), 8-byte stores -------------------------------
+    // (SwiGLU: gate tile ni and up tile ni + TN / 2 hold the same outputs)
+    constexpr int TNO = GLU ? TN / 2 : TN;
+    constexpr int WTNO = GLU ? T::WTN / 2 : T::WTN;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + (size_t)m0 * p.ldc + n0);
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
         const int m = wm * T::WTM + mi * 16 + fa_row;
         const bool m_ok = (m0 + m) < p.M;
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni) {
-            const int n = wn * T::WTN + ni * 16 + 4 * fG;
+        for (int ni = 0; ni < TNO; ++ni) {
+            const int n = wn * WTNO + ni * 16 + 4 * fG;
             const bool ok = m_ok && (n0 + n) < p.N;
-            u32x2 v = {pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]), pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3])};
+            f32x4 h;
+            if constexpr (GLU) {
+                h = swiglu4(acc[ni][mi], acc[ni + TNO][mi]);
+            } else {
+                h = acc[ni][mi];
+            }
+            u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
             buf_store8(rc, ok ? (uint32_t)(m * p.ldc + n) * 2u : kBufInvalid, v);
         }
     }
@@ -337,18 +361,26 @@ TileShape tile_shape(int cfg) {
 }
 
 template <int BM, int BN, int WM, int WN>
-static hipError_t launch_cfg(const TileArgs& a, int grid, hipStream_t s) {
+static hipError_t launch_cfg(const TileArgs& a, int grid, bool glu, hipStream_t s) {
     using T = TileTraits<BM, BN, WM, WN>;
     if (!T::SPLIT && a.sched == kSchedSplitK && a.splits > 1) return hipErrorInvalidValue;
-    tile_gemm_kernel<BM, BN, WM, WN><<<grid, T::NT, T::LDS_BYTES, s>>>(a);
+    if (glu)
+        tile_gemm_kernel<BM, BN, WM, WN, true><<<grid, T::NT, T::LDS_BYTES, s>>>(a);
+    else
+        tile_gemm_kernel<BM, BN, WM, WN, false><<<grid, T::NT, T::LDS_BYTES, s>>>(a);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN>
 static hipError_t configure_cfg() {
-    return hipFuncSetAttribute((const void*)tile_gemm_kernel<BM, BN, WM, WN>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                               TileTraits<BM, BN, WM, WN>::LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)tile_gemm_kernel<BM, BN, WM, WN, false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       TileTraits<BM, BN, WM, WN>::LDS_BYTES);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)tile_gemm_kernel<BM, BN, WM, WN, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                TileTraits<BM, BN, WM, WN>::LDS_BYTES);
+    return e;
 }
 
 hipError_t configure_tile_kernels() {
@@ -357,10 +389,10 @@ hipError_t configure_tile_kernels() {
     return e;
 }
 
-hipError_t launch_tile_gemm(int cfg, const TileArgs& a, int grid, hipStream_t s) {
+hipError_t launch_tile_gemm(int cfg, const TileArgs& a, int grid, bool glu, hipStream_t s) {
     switch (cfg) {
-        case kTile256x256w8: return launch_cfg<256, 256, 2, 4>(a, grid, s);
-        case kTile128x128w4: return launch_cfg<128, 128, 2, 2>(a, grid, s);
+        case kTile256x256w8: return launch_cfg<256, 256, 2, 4>(a, grid, glu, s);
+        case kTile128x128w4: return launch_cfg<128, 128, 2, 2>(a, grid, glu, s);
         default: return hipErrorInvalidValue;
     }
 }

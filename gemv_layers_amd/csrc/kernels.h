@@ -42,13 +42,15 @@ struct TileShape {
     int bm, bn, bk, threads;
 };
 TileShape tile_shape(int cfg);
-hipError_t launch_tile_gemm(int cfg, const TileArgs& a, int grid, hipStream_t s);
+// glu: the SwiGLU form, C = silu(A B[:, :N]) * (A B[:, N:2N]) with B K x 2N (TileArgs.N is the
+// output width N; tiles_n counts BN-wide tiles over the 2N weight columns)
+hipError_t launch_tile_gemm(int cfg, const TileArgs& a, int grid, bool glu, hipStream_t s);
 hipError_t configure_tile_kernels();
 
 // ---- general fallback (any alignment / leading dimension) ----------------------------------
 hipError_t launch_generic_gemm(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M,
                                int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-                               hipStream_t s);
+                               bool glu, hipStream_t s);
 
 // ---- skinny-M weight-streaming GEMM ---------------------------------------------------------
 struct SkinnyArgs {
@@ -69,8 +71,9 @@ struct SkinnyArgs {
 };
 constexpr int kSkinnyStripMin = 128;  // narrowest strip (columns)
 constexpr int kSkinnyStage = 64;    // k rows per streamed unit
-// strip: 128 or 256 columns
-hipError_t launch_skinny_gemm(int mtiles, int strip, const SkinnyArgs& a, hipStream_t s);
+// strip: 128 or 256 columns; glu: the SwiGLU form (strips cover the 2N weight columns, a strip
+// makes strip / 2 outputs; SkinnyArgs.N is the output width N)
+hipError_t launch_skinny_gemm(int mtiles, int strip, bool glu, const SkinnyArgs& a, hipStream_t s);
 hipError_t configure_skinny_kernels();
 int skinny_slot_floats(int mtiles, int strip);  // workspace floats per piece
 

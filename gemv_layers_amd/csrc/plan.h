@@ -12,6 +12,7 @@ enum KernelKind : int { kKernNone = 0, kKernZero = 1, kKernGeneric = 2, kKernTil
 
 struct Plan {
     int kernel = kKernNone;
+    bool glu = false;        // the SwiGLU form: outputs N, weight columns 2N
     // large-tile kernel
     int tile_cfg = 0;
     int bm = 0, bn = 0, bk = 64;
@@ -53,8 +54,10 @@ void wave_efficiency(int64_t ctas, int64_t slots, double* eff, int64_t* waves);
 bool fast_path_ok(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                   int64_t ldb, const void* C, int64_t ldc);
 
-// force: 0 = dispatch on M, 1 = skinny kernel, 2 = large-tile family.
-Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast_ok, int force);
+// force: 0 = dispatch on M, 1 = skinny kernel, 2 = large-tile family. glu: plan the SwiGLU form,
+// whose kernels stream 2N weight columns (gate, then up) for N outputs.
+Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast_ok, int force,
+               bool glu = false);
 
 std::string plan_json(const Plan& p, int64_t M, int64_t N, int64_t K);
 

@@ -1,11 +1,12 @@
 """Summaries of rocprofv3 CSV output for this library's kernels (plain Python, no GPU needed).
 
-    python -m gemv_layers_amd.profiling stats  <run_kernel_stats.csv> [--command CMD]
+    python -m gemv_layers_amd.profiling stats  <run_kernel_stats.csv> [--kernel REGEX] [--command CMD]
     python -m gemv_layers_amd.profiling traffic --fetch <counter_collection.csv>
         --write <counter_collection.csv> --kernel REGEX --copy-bytes N --workload NAME
         [--algorithmic-bytes B] [--command CMD]
 
-`stats` prints the per-kernel table of a `--kernel-trace --stats --output-format csv` run.
+`stats` prints the per-kernel table of a `--kernel-trace --stats --output-format csv` run (the
+kernels matching REGEX only, when given).
 `traffic` turns two counter passes (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, both over a
 command that also runs the library's copy kernel on `--copy-bytes` bytes, e.g.
 `bench.py --copy-calibration`) into HBM bytes per launch of the kernel matching REGEX: each
@@ -71,6 +72,9 @@ def _mean(v: list[float]) -> float:
 
 def cmd_stats(a) -> None:
     rows = kernel_stats(a.csv)
+    if a.kernel:
+        rx = re.compile(a.kernel)
+        rows = [r for r in rows if rx.search(r["name"])]
     if a.command:
         print(f"# command: {a.command}")
     print(f"{'calls':>7} {'avg_us':>11} {'min_us':>10} {'max_us':>10} {'time%':>7}  kernel")
@@ -121,6 +125,7 @@ def main(argv=None) -> None:
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("--top", type=int, default=12)
+    s.add_argument("--kernel", default="")
     s.add_argument("--command", default="")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)

@@ -94,14 +94,45 @@ int gemm_bf16_tiled(int64_t M, int64_t N, int64_t K,
                     gemm_stream_t stream);
 
 /*
+ * gemm_bf16_swiglu: the gate and up projections of a Llama MLP and their SwiGLU in one call:
+ *   C = silu(A * Wg) .* (A * Wu),   silu(x) = x / (1 + e^-x),   .* element by element,
+ * where Wg and Wu are the two halves of one K x 2N weight B: columns 0 .. N-1 are Wg and
+ * columns N .. 2N-1 are Wu (gate and up concatenated along the output dimension). SwiGLU is
+ * silu of the gate times the up projection (spark-kernels post, "the memory-bound kernels",
+ * where it is one kernel instead of PyTorch's two); here it runs in the epilogue of the product
+ * that makes g and u, so g and u stay float32 accumulators and only C is rounded to bf16 (round
+ * to nearest even), once.
+ * Layout: A M x K (lda >= K), B K x 2N (ldb >= 2N), C M x N (ldc >= N), row-major bf16, device
+ * pointers owned by the caller; C must not overlap A or B.
+ * Dispatch as gemm_bf16: M <= 64 streams B once with the skinny kernel, larger M runs the
+ * large-tile kernel; operands the fast kernels cannot take (alignment, N, K or leading
+ * dimensions not multiples of 8) run a general kernel with the same contract.
+ * M == 0 or N == 0: nothing is launched. K == 0: C is set to zero (silu(0) * 0).
+ * Errors: GEMM_ERR_INVALID_ARG for negative sizes, lda < K, ldb < 2N, ldc < N, or a null pointer
+ * with a non-empty extent; GEMM_ERR_NOT_INITIALIZED before gemm_init; GEMM_ERR_HIP if a launch
+ * fails. Deterministic, enqueued on `stream` without synchronising (capturable), and sharing the
+ * device workspace with the other compute calls (concurrent calls must be serialised).
+ */
+int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda,
+                     const void *B, int64_t ldb,
+                     void *C, int64_t ldc,
+                     gemm_stream_t stream);
+
+/* Flags of gemm_plan_describe. */
+#define GEMM_PLAN_SKINNY 1 /* the plan of gemm_bf16_skinny */
+#define GEMM_PLAN_SWIGLU 2 /* the plan of gemm_bf16_swiglu (with GEMM_PLAN_SKINNY: its skinny form) */
+
+/*
  * gemm_plan_describe: host-only. Writes, as a JSON object, the plan the library would use for an
  * M x N x K product on a device with `cus` compute units (tile, grid, schedule, split count,
  * wave count and wave efficiency = (tiles/slots)/ceil(tiles/slots), the quantity of "Kernel
- * development on sm_120", section 4, budget 4). `skinny` selects the skinny entry point's plan.
- * Touches no HIP state. Returns GEMM_ERR_INVALID_ARG for bad sizes or a buffer too small
- * (buf is always NUL-terminated when len > 0).
+ * development on sm_120", section 4, budget 4). `flags` is 0 for gemm_bf16, or a combination of
+ * GEMM_PLAN_SKINNY and GEMM_PLAN_SWIGLU. Touches no HIP state. Returns GEMM_ERR_INVALID_ARG for
+ * bad sizes, unknown flags or a buffer too small (buf is always NUL-terminated when len > 0),
+ * GEMM_ERR_UNSUPPORTED for GEMM_PLAN_SKINNY with M outside 1 .. 64.
  */
-int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int skinny, char *buf, int len);
+int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int flags, char *buf, int len);
 
 /*
  * gemm_wave_efficiency: host-only closed form of "Kernel development on sm_120", section 4,

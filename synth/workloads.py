@@ -10,6 +10,10 @@ row-major.
 Seeds: operand A of workload family ``f`` uses ``0x5EED0000 + 2 f``, operand B
 ``0x5EED0000 + 2 f + 1``. The decode workloads of one weight shape share a family, so the
 M-row activations are the first M rows of the same stream.
+
+The SwiGLU workloads (``glu``) are the gate and up projections of the same MLP in one product:
+B is the K x 2N concatenation of the two 4096 x 11008 weights (gate columns first), C is the
+M x N result silu(A Wg) * (A Wu), at the prefill and decode row counts.
 """
 
 from __future__ import annotations
@@ -29,6 +33,7 @@ class Workload:
     sigma_b: float
     family: int
     bound: str  # "mfma", "hbm" or "latency"
+    glu: bool = False  # SwiGLU form: B is K x 2N (gate, then up), C is M x N
 
     @property
     def seed_a(self) -> int:
@@ -39,13 +44,18 @@ class Workload:
         return SEED_BASE + 2 * self.family + 1
 
     @property
+    def b_cols(self) -> int:
+        """Columns of B: N, or 2N for the SwiGLU form."""
+        return 2 * self.N if self.glu else self.N
+
+    @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        return 2 * self.M * self.b_cols * self.K
 
     @property
     def bytes(self) -> int:
         """Algorithmic bytes: A and B read once, C written once, all bf16."""
-        return 2 * (self.M * self.K + self.K * self.N + self.M * self.N)
+        return 2 * (self.M * self.K + self.K * self.b_cols + self.M * self.N)
 
 
 def _mk():
@@ -61,6 +71,9 @@ def _mk():
         w.append(Workload(f"dec_up_M{m}", m, 11008, 4096, 1.0, 0.02, 6, "hbm"))
     for m in (1, 2, 16, 64):
         w.append(Workload(f"dec_down_M{m}", m, 4096, 11008, 1.0, 0.02, 7, "hbm"))
+    w.append(Workload("glu_prefill", 4096, 11008, 4096, 1.0, 0.02, 8, "mfma", glu=True))
+    for m in (1, 16, 64):
+        w.append(Workload(f"glu_dec_M{m}", m, 11008, 4096, 1.0, 0.02, 9, "hbm", glu=True))
     return {x.name: x for x in w}
 
 

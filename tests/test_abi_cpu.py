@@ -76,3 +76,26 @@ def test_last_plan_buffer_handling():
     buf = ctypes.create_string_buffer(2)
     assert g.lib().gemm_last_plan(buf, 2) in (g.GEMM_OK, g.GEMM_ERR_INVALID_ARG)
     assert g.lib().gemm_last_plan(None, 0) == g.GEMM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,status", [
+    ((8, 8, 8, P, 8, P, 8, P, 8), g.GEMM_ERR_INVALID_ARG),       # ldb < 2N
+    ((8, 8, 8, P, 8, P, 15, P, 8), g.GEMM_ERR_INVALID_ARG),      # ldb = 2N - 1
+    ((8, 8, 8, P, 8, P, 16, P, 7), g.GEMM_ERR_INVALID_ARG),      # ldc < N
+    ((8, 8, 16, P, 8, P, 16, P, 8), g.GEMM_ERR_INVALID_ARG),     # lda < K
+    ((8, 8, 8, P, 8, None, 16, P, 8), g.GEMM_ERR_INVALID_ARG),   # null B
+    ((-1, 8, 8, P, 8, P, 16, P, 8), g.GEMM_ERR_INVALID_ARG),
+    ((8, 2**62, 8, P, 8, P, 2**63 - 1, P, 2**62), g.GEMM_ERR_INVALID_ARG),  # 2N overflows
+    ((0, 8, 8, None, 8, P, 16, None, 8), g.GEMM_OK),             # empty output: no-op
+    ((8, 8, 8, P, 8, P, 16, P, 8), g.GEMM_ERR_NOT_INITIALIZED),  # valid, no gemm_init yet
+])
+def test_swiglu_validation_without_gpu(args, status):
+    assert g.lib().gemm_bf16_swiglu(*args, None) == status
+
+
+def test_plan_describe_flags():
+    buf = ctypes.create_string_buffer(4096)
+    assert g.lib().gemm_plan_describe(4, 64, 64, 256, 4, buf, 4096) == g.GEMM_ERR_INVALID_ARG
+    assert g.lib().gemm_plan_describe(65, 64, 64, 256, 3, buf, 4096) == g.GEMM_ERR_UNSUPPORTED
+    assert g.gemm_plan_describe(4, 64, 64, swiglu=True)["op"] == "swiglu"
+    assert g.gemm_plan_describe(4, 64, 64)["op"] == "gemm"

@@ -128,3 +128,32 @@ def test_dispatch_threshold_and_degenerate():
     assert g.gemm_plan_describe(8, 8, 0, 256)["kernel"] == "zero"
     with pytest.raises(g.GemmError):
         g.gemm_plan_describe(65, 8, 8, 256, skinny=True)
+
+
+# ---- the SwiGLU form: the fast kernels are planned over the 2N weight columns --------------
+
+@pytest.mark.parametrize("M,N,K", [(4096, 11008, 4096), (1000, 1000, 1000), (300, 520, 328)])
+def test_swiglu_tile_plan_covers_both_halves(M, N, K):
+    p = g.gemm_plan_describe(M, N, K, swiglu=True)
+    q = g.gemm_plan_describe(M, 2 * N, K)
+    assert p["kernel"] == "tile" and p["op"] == "swiglu" and p["N"] == N
+    for key in ("bm", "bn", "tiles_m", "tiles_n", "grid", "splits", "schedule"):
+        assert p[key] == q[key], key
+    # a BN-wide tile makes BN / 2 outputs
+    assert p["tiles_n"] == _cdiv(N, p["bn"] // 2)
+
+
+@pytest.mark.parametrize("M", [1, 2, 16, 17, 64])
+def test_swiglu_skinny_plan_covers_both_halves(M):
+    N, K = 11008, 4096
+    p = g.gemm_plan_describe(M, N, K, swiglu=True)
+    q = g.gemm_plan_describe(M, 2 * N, K)
+    assert p["kernel"] == "skinny" and p["op"] == "swiglu"
+    assert p["ks"] == q["ks"] and p["mtiles"] == q["mtiles"]
+    assert p["strips"] == _cdiv(N, p["strip"] // 2)
+    assert p["grid"] == q["grid"]  # the same aligned grid, or Stream-K over every CU
+    # a grid tie goes to the wider strip: gate and up segments of a row stay 256 bytes
+    if M <= 32:
+        assert (p["strip"], p["grid"]) == (256, 172) and (q["strip"], q["grid"]) == (128, 172)
+    else:
+        assert p["strip"] == q["strip"] == 128 and p["grid"] == 256

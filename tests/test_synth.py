@@ -61,4 +61,6 @@ def test_workloads():
     assert w["dec_down_M64"].K == 11008 and w["dec_up_M1"].N == 11008
     assert w["sq4096"].flops == 2 * 4096 ** 3
     assert w["dec_up_M1"].bytes == 2 * (4096 + 4096 * 11008 + 11008)
-    assert len({(x.seed_a, x.seed_b) for x in w.values()}) == 8
+    assert len({(x.seed_a, x.seed_b) for x in w.values()}) == 10
+    assert w["glu_prefill"].b_cols == 2 * 11008 and w["glu_prefill"].flops == 2 * 4096 * 22016 * 4096
+    assert w["glu_dec_M1"].bytes == 2 * (4096 + 4096 * 22016 + 11008)
