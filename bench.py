@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--no-torch", action="store_true", help="skip the torch.matmul comparison")
     ap.add_argument("--no-swiglu", action="store_true",
                     help="skip the fused gate/up SwiGLU workloads")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the block-scaled (MXFP8 x MXFP4) decode workloads")
     ap.add_argument("--swiglu-unfused-ours", action="store_true",
                     help="also time the unfused SwiGLU path on this library's own product (it runs "
                          "the plain kernels, which then also appear in a profile of this command)")
@@ -493,6 +495,106 @@ def main():
             glu[name] = rec
             del Bs, b0, Ag, Hg, Gu, Hu
         out["swiglu"] = glu
+
+    # ---------------- block-scaled decode (MXFP8 activations x MXFP4 weights) ----------------
+    # the decode shapes with the weight in the nn.Linear layout (N x K) packed to MXFP4 once;
+    # timed on pre-quantised activations (the product alone) and from bf16 activations
+    # (quantisation launch + product), 16 rotated weight copies (384 MB) so every call reads cold
+    if not args.no_mx:
+        mxd = {}
+        copies = 16
+        packed = {}
+        for name in ("dec_up_M1", "dec_up_M16", "dec_up_M64", "dec_down_M1", "dec_down_M64"):
+            wd = WORKLOADS[name]
+            M, N, K = wd.M, wd.N, wd.K
+            log(f"mx {name}")
+            if (N, K) not in packed:
+                packed.clear()
+                W = dev(matrix("normal", N, K, seed=wd.seed_b, sigma=wd.sigma_b))
+                wb, sb = g.gemm_mx_packed_sizes(N, K)
+                wp0 = torch.empty(wb, dtype=torch.uint8, device="cuda")
+                sp0 = torch.empty(sb, dtype=torch.uint8, device="cuda")
+                g.gemm_mx_pack_weight(N, K, P(W), K, P(wp0), P(sp0), sh)
+                del W
+                packed[(N, K)] = ([wp0] + [wp0.clone() for _ in range(copies - 1)],
+                                  [sp0] + [sp0.clone() for _ in range(copies - 1)], wb, sb)
+            wps, sps, wb, sb = packed[(N, K)]
+            Ad = dev(matrix("normal", M, K, seed=wd.seed_a, sigma=wd.sigma_a))
+            aq = torch.empty(M * K, dtype=torch.uint8, device="cuda")
+            asc = torch.empty(M * K // 32, dtype=torch.uint8, device="cuda")
+            g.gemm_mx_quantize_act(M, K, P(Ad), K, P(aq), K, P(asc), K // 32, sh)
+            Cd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+            def b2b_us(fn, n=160):
+                for i in range(2 * copies):
+                    fn(i % copies)
+                torch.cuda.synchronize()
+                e0, e1 = events(2)
+                e0.record(stream)
+                for i in range(n):
+                    fn(i % copies)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / n
+
+            def mx_call(i):
+                g.gemm_mx_decode(M, N, K, P(aq), K, P(asc), K // 32, P(wps[i]), P(sps[i]), P(Cd), N,
+                                 g.current_stream_handle())
+
+            def mx_bf16_call(i):
+                g.gemm_mx_decode_bf16(M, N, K, P(Ad), K, P(wps[i]), P(sps[i]), P(Cd), N,
+                                      g.current_stream_handle())
+
+            def graph_us(fn, reps=10):
+                """Per call, the calls over every weight copy captured once and replayed: the
+                device time back to back, without the host's per-call cost (a call here takes
+                about as long to issue from Python as the kernel takes to run)."""
+                side = torch.cuda.Stream()
+                side.wait_stream(stream)
+                with torch.cuda.stream(side):
+                    fn(0)
+                stream.wait_stream(side)
+                torch.cuda.synchronize()
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    for i in range(copies):
+                        fn(i)
+                gr.replay()
+                torch.cuda.synchronize()
+                e0, e1 = events(2)
+                e0.record(stream)
+                for _ in range(reps):
+                    gr.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                del gr
+                return e0.elapsed_time(e1) * 1e3 / (reps * copies)
+
+            us_eager = b2b_us(lambda i: g.gemm_mx_decode(M, N, K, P(aq), K, P(asc), K // 32, P(wps[i]),
+                                                         P(sps[i]), P(Cd), N, sh))
+            plan = g.gemm_last_plan()
+            us = graph_us(mx_call)
+            us_q = graph_us(mx_bf16_call)
+            nbytes = wb + sb + M * K + M * K // 32 + 2 * M * N
+            gbps = nbytes / (us * 1e-6) / 1e9
+            rec = {"M": M, "N": N, "K": K, "us_graph_replay": round(us, 2),
+                   "us_eager_back_to_back": round(us_eager, 2),
+                   "us_with_activation_quantisation_graph_replay": round(us_q, 2),
+                   "algorithmic_bytes": nbytes, "gbps": round(gbps, 1),
+                   "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0,
+                                "unit": "GB/s", "frac": round(gbps / 8000.0, 4)},
+                   "splits": plan.get("splits"), "grid": plan.get("grid")}
+            if "hbm_copy_gbps" in peaks:
+                rec["frac_of_measured_copy"] = round(gbps / peaks["hbm_copy_gbps"], 4)
+            bf = out.get("decode", {}).get(name, {}).get("us_graph_replay")
+            if bf:
+                rec["bf16_skinny_us_graph_replay"] = bf
+                rec["speedup_vs_bf16"] = round(bf / us, 3)
+                rec["speedup_vs_bf16_with_quantisation"] = round(bf / us_q, 3)
+            mxd[name] = rec
+            del Ad, aq, asc, Cd
+        del packed
+        out["mx_decode"] = mxd
 
     # ---------------- more compute-bound workloads ----------------
     if args.large:

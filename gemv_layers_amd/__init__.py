@@ -25,6 +25,7 @@ GEMM_ERR_HIP = 4
 
 GEMM_PLAN_SKINNY = 1
 GEMM_PLAN_SWIGLU = 2
+GEMM_PLAN_MX = 4
 
 # every symbol include/gemm_bf16.h declares
 EXPORTS = (
@@ -34,6 +35,8 @@ EXPORTS = (
     "gemm_peak_mfma_launch", "gemm_peak_copy_launch", "gemm_peak_read_launch",
     "gemm_peak_clock_launch",
     "gemm_peak_empty_launch", "gemm_fill_launch",
+    "gemm_mx_packed_sizes", "gemm_mx_pack_weight", "gemm_mx_quantize_act", "gemm_mx_decode",
+    "gemm_mx_decode_bf16",
 )
 
 
@@ -85,6 +88,16 @@ def lib() -> ctypes.CDLL:
     L.gemm_peak_empty_launch.restype = i32
     L.gemm_fill_launch.argtypes = [p, i64, u32, p]
     L.gemm_fill_launch.restype = i32
+    L.gemm_mx_packed_sizes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    L.gemm_mx_packed_sizes.restype = i32
+    L.gemm_mx_pack_weight.argtypes = [i64, i64, p, i64, p, p, p]
+    L.gemm_mx_pack_weight.restype = i32
+    L.gemm_mx_quantize_act.argtypes = [i64, i64, p, i64, p, i64, p, i64, p]
+    L.gemm_mx_quantize_act.restype = i32
+    L.gemm_mx_decode.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, p, i64, p]
+    L.gemm_mx_decode.restype = i32
+    L.gemm_mx_decode_bf16.argtypes = [i64, i64, i64, p, i64, p, p, p, i64, p]
+    L.gemm_mx_decode_bf16.restype = i32
     _lib = L
     return L
 
@@ -133,11 +146,35 @@ def gemm_bf16_swiglu(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
 
 
 def gemm_plan_describe(M: int, N: int, K: int, cus: int = 256, skinny: bool = False,
-                       swiglu: bool = False) -> dict:
+                       swiglu: bool = False, mx: bool = False) -> dict:
     buf = ctypes.create_string_buffer(4096)
-    flags = (GEMM_PLAN_SKINNY if skinny else 0) | (GEMM_PLAN_SWIGLU if swiglu else 0)
+    flags = ((GEMM_PLAN_SKINNY if skinny else 0) | (GEMM_PLAN_SWIGLU if swiglu else 0)
+             | (GEMM_PLAN_MX if mx else 0))
     _check("gemm_plan_describe", lib().gemm_plan_describe(M, N, K, cus, flags, buf, 4096))
     return json.loads(buf.value.decode())
+
+
+def gemm_mx_packed_sizes(N: int, K: int) -> tuple[int, int]:
+    """(code bytes, scale bytes) of the packed MXFP4 form of an N x K weight."""
+    w, s = ctypes.c_int64(), ctypes.c_int64()
+    _check("gemm_mx_packed_sizes", lib().gemm_mx_packed_sizes(N, K, ctypes.byref(w), ctypes.byref(s)))
+    return w.value, s.value
+
+
+def gemm_mx_pack_weight(N, K, W, ldw, Wp, Sp, stream=None) -> None:
+    _check("gemm_mx_pack_weight", lib().gemm_mx_pack_weight(N, K, W, ldw, Wp, Sp, stream))
+
+
+def gemm_mx_quantize_act(M, K, A, lda, Aq, ldaq, As, ldas, stream=None) -> None:
+    _check("gemm_mx_quantize_act", lib().gemm_mx_quantize_act(M, K, A, lda, Aq, ldaq, As, ldas, stream))
+
+
+def gemm_mx_decode(M, N, K, Aq, ldaq, As, ldas, Wp, Sp, C, ldc, stream=None) -> None:
+    _check("gemm_mx_decode", lib().gemm_mx_decode(M, N, K, Aq, ldaq, As, ldas, Wp, Sp, C, ldc, stream))
+
+
+def gemm_mx_decode_bf16(M, N, K, A, lda, Wp, Sp, C, ldc, stream=None) -> None:
+    _check("gemm_mx_decode_bf16", lib().gemm_mx_decode_bf16(M, N, K, A, lda, Wp, Sp, C, ldc, stream))
 
 
 def gemm_wave_efficiency(ctas: int, slots: int):

@@ -20,6 +20,10 @@ constexpr int kMaxDevices = 64;
 // Workspace per device: float32 partial slots for split tiles / K slices, and their counters.
 constexpr int64_t kWsFloats = int64_t(32) << 20;  // 128 MiB
 constexpr int64_t kWsCounters = int64_t(1) << 16;
+// The last 16 MiB of the workspace hold the MXFP8 activations that gemm_mx_decode_bf16 quantises
+// before its product; MX plans keep their partial slots below them.
+constexpr int64_t kMxActBytes = int64_t(16) << 20;
+constexpr int64_t kMxPartialFloats = kWsFloats - kMxActBytes / 4;
 
 struct DeviceState {
     bool ready = false;
@@ -145,6 +149,107 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
 
 }  // namespace
 
+// ---- block-scaled (MX) decode -------------------------------------------------------------------
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// the device state of the current device, or nullptr
+DeviceState* current_state(int* status) {
+    if (g_ready_count == 0) {
+        *status = GEMM_ERR_NOT_INITIALIZED;
+        return nullptr;
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *status = GEMM_ERR_HIP;
+        return nullptr;
+    }
+    if (!g_dev[dev].ready) {
+        *status = GEMM_ERR_NOT_INITIALIZED;
+        return nullptr;
+    }
+    return &g_dev[dev];
+}
+
+int mx_packed(int64_t N, int64_t K, int64_t* wbytes, int64_t* sbytes) {
+    if (N < 0 || K < 0 || (N % 16) || (K % 128)) return GEMM_ERR_INVALID_ARG;
+    const int64_t ks = K / 128, kq = (ks + 3) / 4;
+    *wbytes = (N / 16) * ks * 1024;
+    *sbytes = (N / 16) * kq * 256;
+    if (*wbytes > INT32_MAX || *sbytes > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
+    return GEMM_OK;
+}
+
+int mx_quantize_act(int64_t M, int64_t K, const void* A, int64_t lda, void* Aq, int64_t ldaq, void* As,
+                    int64_t ldas, hipStream_t stream) {
+    if (M < 0 || K < 0 || (K % 32) || lda < K || ldaq < K || ldas < K / 32) return GEMM_ERR_INVALID_ARG;
+    if (M > 0 && K > 0 && (!A || !Aq || !As)) return GEMM_ERR_INVALID_ARG;
+    if (!aligned(A, 16) || !aligned(Aq, 16) || (lda % 8) || (ldaq % 16)) return GEMM_ERR_INVALID_ARG;
+    if (M > INT32_MAX || lda > INT32_MAX || ldaq > INT32_MAX || ldas > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
+    if (M == 0 || K == 0) return GEMM_OK;
+    int st = GEMM_OK;
+    if (!current_state(&st)) return st;
+    return glk::launch_mx_quant(false, static_cast<const uint16_t*>(A), (int)M, (int)K, (int)lda,
+                                static_cast<uint8_t*>(Aq), (int)ldaq, static_cast<uint8_t*>(As), (int)ldas,
+                                stream) == hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
+int mx_decode(int64_t M, int64_t N, int64_t K, const void* Aq, int64_t ldaq, const void* As, int64_t ldas,
+              const void* Wp, const void* Sp, void* C, int64_t ldc, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || ldaq < K || ldas < K / 32 || ldc < N) return GEMM_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && !C) return GEMM_ERR_INVALID_ARG;
+    if (M > 0 && K > 0 && (!Aq || !As)) return GEMM_ERR_INVALID_ARG;
+    if (N > 0 && K > 0 && (!Wp || !Sp)) return GEMM_ERR_INVALID_ARG;
+    if (M > 64 || (N % 16) || (K % 128)) return GEMM_ERR_UNSUPPORTED;
+    if (!aligned(Aq, 16) || !aligned(Wp, 16) || !aligned(C, 8) || (ldaq % 16) || (ldc % 4))
+        return GEMM_ERR_INVALID_ARG;
+    int64_t wb = 0, sb = 0;
+    int st = mx_packed(N, K, &wb, &sb);
+    if (st != GEMM_OK) return st;
+    if (64 * ldaq > INT32_MAX || 64 * ldas > INT32_MAX || ldc > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return GEMM_OK;
+    DeviceState* ds = current_state(&st);
+    if (!ds) return st;
+    glk::DeviceInfo info = ds->info;
+    info.ws_floats = kMxPartialFloats;
+    const glk::Plan p = glk::make_mx_plan(M, N, K, info);
+    hipError_t e = hipSuccess;
+    if (p.kernel == glk::kKernZero) {
+        e = glk::launch_zero_c(static_cast<uint16_t*>(C), M, N, ldc, stream);
+    } else {
+        glk::MxArgs a;
+        a.Aq = static_cast<const uint8_t*>(Aq);
+        a.As = static_cast<const uint8_t*>(As);
+        a.Wp = static_cast<const uint8_t*>(Wp);
+        a.Sp = static_cast<const uint8_t*>(Sp);
+        a.C = static_cast<uint16_t*>(C);
+        a.M = (int)M;
+        a.N = (int)N;
+        a.K = (int)K;
+        a.ldaq = (int)ldaq;
+        a.ldas = (int)ldas;
+        a.ldc = (int)ldc;
+        a.tiles = (int)(N / 16);
+        a.ks = (int)(K / 128);
+        a.kq = (a.ks + 3) / 4;
+        a.pieces = p.splits;
+        a.nxcd = p.nxcd;
+        a.ws = ds->ws;
+        a.counters = ds->counters;
+        e = glk::launch_mx_decode(p.mtiles, a, (int)p.grid, stream);
+    }
+    if (e != hipSuccess) return GEMM_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_last_plan = glk::plan_json(p, M, N, K);
+    return GEMM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int gemm_init(int device) {
@@ -175,6 +280,7 @@ int gemm_init(int device) {
         rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_skinny_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_tile_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
+    if (rc == GEMM_OK && glk::configure_mx_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && hipDeviceSynchronize() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK) {
         ds.ready = true;
@@ -210,7 +316,17 @@ int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
 }
 
 int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int flags, char* buf, int len) {
-    if (M < 0 || N < 0 || K < 0 || cus <= 0 || (flags & ~3)) return GEMM_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || cus <= 0 || (flags & ~7)) return GEMM_ERR_INVALID_ARG;
+    if (flags & GEMM_PLAN_MX) {
+        if (flags != GEMM_PLAN_MX) return GEMM_ERR_INVALID_ARG;
+        if (M > 64 || (N % 16) || (K % 128)) return GEMM_ERR_UNSUPPORTED;
+        glk::DeviceInfo dev;
+        dev.cus = cus;
+        dev.nxcd = (cus % 8 == 0) ? 8 : 1;
+        dev.ws_floats = kMxPartialFloats;
+        dev.ws_counters = kWsCounters;
+        return copy_out(glk::plan_json(glk::make_mx_plan(M, N, K, dev), M, N, K), buf, len);
+    }
     const bool skinny = (flags & GEMM_PLAN_SKINNY) != 0, glu = (flags & GEMM_PLAN_SWIGLU) != 0;
     if (glu && N > INT64_MAX / 2) return GEMM_ERR_INVALID_ARG;
     if (skinny && (M < 1 || M > 64)) return GEMM_ERR_UNSUPPORTED;
@@ -263,6 +379,61 @@ int gemm_finalize(void) {
     }
     g_ready_count = 0;
     return rc;
+}
+
+
+int gemm_mx_packed_sizes(int64_t N, int64_t K, int64_t* wp_bytes, int64_t* sp_bytes) {
+    if (!wp_bytes || !sp_bytes) return GEMM_ERR_INVALID_ARG;
+    return mx_packed(N, K, wp_bytes, sp_bytes);
+}
+
+int gemm_mx_pack_weight(int64_t N, int64_t K, const void* W, int64_t ldw, void* Wp, void* Sp,
+                        gemm_stream_t stream) {
+    int64_t wb = 0, sb = 0;
+    int st = mx_packed(N, K, &wb, &sb);
+    if (st != GEMM_OK) return st;
+    if (ldw < K || (N > 0 && K > 0 && (!W || !Wp || !Sp))) return GEMM_ERR_INVALID_ARG;
+    if (!aligned(W, 16) || !aligned(Wp, 16) || (ldw % 8)) return GEMM_ERR_INVALID_ARG;
+    if (N > INT32_MAX || ldw > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
+    if (N == 0 || K == 0) return GEMM_OK;
+    if (!current_state(&st)) return st;
+    return glk::launch_mx_quant(true, static_cast<const uint16_t*>(W), (int)N, (int)K, (int)ldw,
+                                static_cast<uint8_t*>(Wp), 0, static_cast<uint8_t*>(Sp), 0,
+                                reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
+int gemm_mx_quantize_act(int64_t M, int64_t K, const void* A, int64_t lda, void* Aq, int64_t ldaq, void* As,
+                         int64_t ldas, gemm_stream_t stream) {
+    return mx_quantize_act(M, K, A, lda, Aq, ldaq, As, ldas, reinterpret_cast<hipStream_t>(stream));
+}
+
+int gemm_mx_decode(int64_t M, int64_t N, int64_t K, const void* Aq, int64_t ldaq, const void* As,
+                   int64_t ldas, const void* Wp, const void* Sp, void* C, int64_t ldc, gemm_stream_t stream) {
+    return mx_decode(M, N, K, Aq, ldaq, As, ldas, Wp, Sp, C, ldc, reinterpret_cast<hipStream_t>(stream));
+}
+
+int gemm_mx_decode_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* Wp,
+                        const void* Sp, void* C, int64_t ldc, gemm_stream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldc < N) return GEMM_ERR_INVALID_ARG;
+    if (M > 64 || (N % 16) || (K % 128)) return GEMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (M > 0 && K > 0 && !A) return GEMM_ERR_INVALID_ARG;
+    if (K == 0) return mx_decode(M, N, K, nullptr, 0, nullptr, 0, Wp, Sp, C, ldc, reinterpret_cast<hipStream_t>(stream));
+    int st = GEMM_OK;
+    DeviceState* ds = current_state(&st);
+    if (!ds) return st;
+    // the quantised activations go to the workspace tail (both launches on the same stream)
+    const int64_t ldaq = (K + 15) / 16 * 16, ldas = K / 32;
+    if (M * ldaq + M * ldas + 16 > kMxActBytes) return GEMM_ERR_UNSUPPORTED;
+    uint8_t* base = reinterpret_cast<uint8_t*>(ds->ws + kMxPartialFloats);
+    uint8_t* aq = base;
+    uint8_t* as = base + (M * ldaq + 15) / 16 * 16;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    st = mx_quantize_act(M, K, A, lda, aq, ldaq, as, ldas, s);
+    if (st != GEMM_OK) return st;
+    return mx_decode(M, N, K, aq, ldaq, as, ldas, Wp, Sp, C, ldc, s);
 }
 
 int gemm_peak_mfma_launch(int64_t iters, int blocks, float* sink, uint64_t* cycles,

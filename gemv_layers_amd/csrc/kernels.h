@@ -77,6 +77,33 @@ hipError_t launch_skinny_gemm(int mtiles, int strip, bool glu, const SkinnyArgs&
 hipError_t configure_skinny_kernels();
 int skinny_slot_floats(int mtiles, int strip);  // workspace floats per piece
 
+// ---- block-scaled (MX) decode product ------------------------------------------------------
+// C = deq(Aq) * deq(W)^T: Aq MXFP8 (E4M3, M x K row-major, ldaq bytes per row; scales M x K/32,
+// ldas bytes per row), W MXFP4 in the packed layout (codes Wp, scales Sp; see gemm_mx.hip).
+struct MxArgs {
+    const uint8_t* Aq;
+    const uint8_t* As;
+    const uint8_t* Wp;
+    const uint8_t* Sp;
+    uint16_t* C;
+    int M, N, K;
+    int ldaq, ldas, ldc;
+    int tiles;           // N / 16 column tiles
+    int ks, kq;          // K / 128 k-steps; ceil(ks / 4) scale groups
+    int pieces;          // K pieces per group of mx_decode_tiles_per_group() tiles (one workgroup each)
+    int nxcd;            // XCDs the hardware deals workgroups over (1 = no remap)
+    float* ws;           // pieces > 1: groups * pieces * 4 * mtiles * 256 floats
+    uint32_t* counters;  // one per group, zero between launches
+};
+int mx_decode_tiles_per_group();
+int mx_decode_lds_bytes(int mtiles);
+hipError_t configure_mx_kernels();
+hipError_t launch_mx_decode(int mtiles, const MxArgs& a, int grid, hipStream_t s);
+// bf16 rows -> MX codes and scales: fp4 = false, E4M3 row-major (Q: ldq bytes per row, S: lds);
+// fp4 = true, E2M1 in the packed weight layout (rows % 16 == 0, cols % 128 == 0; ldq, lds unused)
+hipError_t launch_mx_quant(bool fp4, const uint16_t* X, int rows, int cols, int ldx, uint8_t* Q, int ldq,
+                           uint8_t* S, int lds, hipStream_t s);
+
 // ---- misc ------------------------------------------------------------------------------------
 hipError_t launch_zero_c(uint16_t* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
 hipError_t launch_fill(void* dst, int64_t bytes, uint32_t value, hipStream_t s);

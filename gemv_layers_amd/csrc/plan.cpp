@@ -211,6 +211,52 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast
     return q;
 }
 
+// Block-scaled decode: a workgroup streams the packed weights of 4 column tiles (64 columns) over
+// one of S pieces of K, its 4 waves each holding a few k-steps of loads in flight in registers.
+// Splitting K costs a float32 fixup (about 2.4 us per call on the 11008 x 4096 weight, measured),
+// so S is the smallest count whose grid covers 60% of the CUs: S = 1 for the 172 groups of an
+// 11008-wide weight (8.3 us at M = 1 against 10.7 at S = 2), S = 3 for the 64 groups of a
+// 4096-wide one (10.3 us, against 15.0 at S = 1 and 12.2 at S = 8). Every wave keeps at least one
+// k-step.
+Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+    Plan p;
+    p.kernel = kKernMx;
+    if (M == 0 || N == 0) {
+        p.kernel = kKernNone;
+        p.reason = "empty output";
+        return p;
+    }
+    if (K == 0) {
+        p.kernel = kKernZero;
+        p.grid = 1;
+        p.reason = "K == 0: C is the empty sum";
+        return p;
+    }
+    p.nxcd = dev.nxcd;
+    p.threads = 256;
+    p.mtiles = (int)cdiv(M, 16);
+    p.tiles_n = N / 16;
+    const int tpg = mx_decode_tiles_per_group();
+    p.strips = (int)cdiv(p.tiles_n, tpg);
+    p.strip = 16 * tpg;
+    p.ks = (int)(K / 128);
+    const int64_t per_cu = p.mtiles <= 2 ? 2 : 1;  // waves' registers: two workgroups per CU
+    p.slots = per_cu * dev.cus;
+    int64_t s = std::max<int64_t>(1, cdiv(3 * (int64_t)dev.cus, 5 * p.strips));
+    s = std::min<int64_t>(s, std::max<int64_t>(1, p.ks / 4));
+    const int64_t slot_floats = (int64_t)tpg * p.mtiles * 256;
+    while (s > 1 && p.strips * s * slot_floats > dev.ws_floats) --s;
+    if (s > 1 && p.strips > dev.ws_counters) s = 1;
+    p.splits = (int)s;
+    p.grid = p.strips * s;
+    p.ws_floats = s > 1 ? p.strips * s * slot_floats : 0;
+    p.counters = s > 1 ? p.strips : 0;
+    finish_waves(p);
+    p.reason = "MXFP8 x MXFP4 decode: " + std::to_string(p.strips) + " groups of " +
+               std::to_string(tpg) + " column tiles, K in " + std::to_string(s) + " pieces";
+    return p;
+}
+
 static const char* kernel_name(int k) {
     switch (k) {
         case kKernNone: return "none";
@@ -218,6 +264,7 @@ static const char* kernel_name(int k) {
         case kKernGeneric: return "generic";
         case kKernTile: return "tile";
         case kKernSkinny: return "skinny";
+        case kKernMx: return "mx";
         default: return "?";
     }
 }
@@ -234,10 +281,11 @@ std::string plan_json(const Plan& p, int64_t M, int64_t N, int64_t K) {
              (long long)M, (long long)N, (long long)K, kernel_name(p.kernel), p.bm, p.bn, p.bk,
              p.threads, (long long)p.tiles_m, (long long)p.tiles_n, (long long)p.tiles,
              p.kernel == kKernTile ? (p.sched == kSchedSplitK ? "split-k" : "data-parallel")
-                                   : (p.kernel == kKernSkinny ? "strips" : "-"),
+                                   : (p.kernel == kKernSkinny || p.kernel == kKernMx ? "strips" : "-"),
              p.splits, p.kt_per_split, p.group_m, p.nxcd, p.mtiles, p.strip, p.strips, p.ks,
              (long long)p.grid, (long long)p.slots, (long long)p.waves, p.wave_eff,
-             (long long)p.ws_floats, p.glu ? "swiglu" : "gemm", p.reason.c_str());
+             (long long)p.ws_floats, p.kernel == kKernMx ? "mx" : (p.glu ? "swiglu" : "gemm"),
+             p.reason.c_str());
     return std::string(buf);
 }
 

@@ -8,7 +8,9 @@
 
 namespace glk {
 
-enum KernelKind : int { kKernNone = 0, kKernZero = 1, kKernGeneric = 2, kKernTile = 3, kKernSkinny = 4 };
+enum KernelKind : int {
+    kKernNone = 0, kKernZero = 1, kKernGeneric = 2, kKernTile = 3, kKernSkinny = 4, kKernMx = 5
+};
 
 struct Plan {
     int kernel = kKernNone;
@@ -58,6 +60,10 @@ bool fast_path_ok(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, c
 // whose kernels stream 2N weight columns (gate, then up) for N outputs.
 Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast_ok, int force,
                bool glu = false);
+
+// The block-scaled decode product (1 <= M <= 64, N % 16 == 0, K % 128 == 0): groups of column
+// tiles (strips) times K pieces (splits), one workgroup each.
+Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
 
 std::string plan_json(const Plan& p, int64_t M, int64_t N, int64_t K);
 

@@ -30,6 +30,9 @@ TILE_SOURCES = ("gemv_layers_amd/csrc/gemm_tile.hip", "gemv_layers_amd/csrc/comm
                 "gemv_layers_amd/csrc/kernels.h", "gemv_layers_amd/csrc/stream_k.h")
 SKINNY_SOURCES = ("gemv_layers_amd/csrc/gemm_skinny.hip", "gemv_layers_amd/csrc/common.h",
                   "gemv_layers_amd/csrc/kernels.h", "gemv_layers_amd/csrc/stream_k.h")
+MX_SOURCES = ("gemv_layers_amd/csrc/gemm_mx.hip", "gemv_layers_amd/csrc/common.h",
+              "gemv_layers_amd/csrc/kernels.h")
+_SOURCES = {"tile": TILE_SOURCES, "skinny": SKINNY_SOURCES, "mx": MX_SOURCES}
 COPY_KERNEL = r"peak_copy_kernel"
 
 
@@ -53,13 +56,15 @@ def kernel_stats(path: str) -> list[dict]:
     return rows
 
 
-def counter_per_dispatch(path: str, counter: str, kernel_regex: str) -> list[float]:
-    """Values of `counter` for every dispatch whose kernel name matches `kernel_regex`."""
+def counter_per_dispatch(path: str, counter: str, kernel_regex: str, grid: int = 0) -> list[float]:
+    """Values of `counter` for every dispatch whose kernel name matches `kernel_regex` (and whose
+    grid has `grid` threads, when given)."""
     rx = re.compile(kernel_regex)
     out = []
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
-            if r["Counter_Name"] == counter and rx.search(r["Kernel_Name"]):
+            if r["Counter_Name"] == counter and rx.search(r["Kernel_Name"]) and \
+                    (not grid or int(r["Grid_Size"]) == grid):
                 out.append(float(r["Counter_Value"]))
     return out
 
@@ -88,19 +93,21 @@ def cmd_traffic(a) -> None:
     kib = 1024.0
     f_copy = _mean(counter_per_dispatch(a.fetch, "FETCH_SIZE", COPY_KERNEL))
     w_copy = _mean(counter_per_dispatch(a.write, "WRITE_SIZE", COPY_KERNEL))
-    f_k = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
-    w_k = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    f_k = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel, a.grid)
+    w_k = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel, a.grid)
     fetch_scale = a.copy_bytes / (f_copy * kib)
     write_scale = a.copy_bytes / (w_copy * kib)
     fetch_b = _mean(f_k) * kib * fetch_scale
     write_b = _mean(w_k) * kib * write_scale
-    srcs = SKINNY_SOURCES if a.sources == "skinny" else TILE_SOURCES
+    srcs = _SOURCES[a.sources]
     print(f"# HBM traffic per launch of the kernel matching /{a.kernel}/ on workload {a.workload}")
     if a.command:
         for ln in a.command.split(" ;; "):
             print(f"# command: {ln}")
     print(f"workload: {a.workload}")
     print(f"kernel_regex: {a.kernel}")
+    if a.grid:
+        print(f"grid_threads: {a.grid}")
     print(f"sources: {' '.join(srcs)}")
     print(f"source_sha256: {source_digest(srcs)}")
     print(f"copy_kernel_bytes_each_way: {a.copy_bytes}")
@@ -133,7 +140,8 @@ def main(argv=None) -> None:
     t.add_argument("--kernel", required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--workload", required=True)
-    t.add_argument("--sources", choices=("tile", "skinny"), default="tile")
+    t.add_argument("--sources", choices=("tile", "skinny", "mx"), default="tile")
+    t.add_argument("--grid", type=int, default=0, help="only dispatches with this many threads")
     t.add_argument("--algorithmic-bytes", type=int, default=0)
     t.add_argument("--command", default="")
     a = ap.parse_args(argv)

@@ -119,18 +119,85 @@ int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K,
                      void *C, int64_t ldc,
                      gemm_stream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Block-scaled (MX) decode: the decode product with weights in MXFP4 and activations in MXFP8,
+ * on gfx950's scaled matrix instructions. Formats are those of the OCP Microscaling (MX)
+ * specification v1.0: a block of 32 consecutive elements along K shares one E8M0 scale byte e
+ * (value 2^(e - 127)); elements are E2M1 (FP4: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives) or E4M3
+ * (FP8, largest 448). The weights are the bytes that bound decode (spark-kernels post, "the
+ * decode kernel"); in MXFP4 they take 0.53 bytes per element instead of bf16's 2. The pages
+ * measure block-scaled GEMMs on pre-quantized operands ("Benchmarks" page of gemm3,
+ * "Implementations"); here the conversions are entry points of their own.
+ * Conversion of a block (both formats): shared exponent floor(log2(max |v|)) - emax (emax 2 for
+ * E2M1, 8 for E4M3), clamped to [-127, 127]; elements v / 2^exponent rounded to the element
+ * format, nearest with ties to even, saturating at its largest magnitude; an all-zero block
+ * gets scale byte 0. Deterministic, bit for bit.
+ * ------------------------------------------------------------------------------------------ */
+
+/*
+ * gemm_mx_packed_sizes: host-only. Bytes of the packed MXFP4 weight codes (*wp_bytes) and scales
+ * (*sp_bytes) of an N x K weight. Requires N % 16 == 0 and K % 128 == 0 (GEMM_ERR_INVALID_ARG
+ * otherwise); GEMM_ERR_UNSUPPORTED when either exceeds 2^31 - 1 bytes.
+ */
+int gemm_mx_packed_sizes(int64_t N, int64_t K, int64_t *wp_bytes, int64_t *sp_bytes);
+
+/*
+ * gemm_mx_pack_weight: converts a bf16 weight W (N x K row-major, the nn.Linear layout: row n
+ * holds the K inputs of output n; ldw >= K, ldw % 8 == 0, W 16-byte aligned) to MXFP4 in the
+ * packed layout the decode product reads (Wp 16-byte aligned, Sp; sizes from
+ * gemm_mx_packed_sizes; both device memory owned by the caller). Layout: column tile t (rows
+ * 16 t .. 16 t + 15) and k-step s (k = 128 s .. 128 s + 127) are the 1024 bytes at
+ * Wp + 1024 (t * K/128 + s); in them bytes 16 l .. 16 l + 15 (l = 0 .. 63) hold the codes of row
+ * 16 t + l % 16 at k = 128 s + 32 (l / 16) + j, j = 0 .. 31, two per byte, even j in the low
+ * nibble. The scale of that 32-element block is Sp[256 (t * ceil(K/512) + s / 4) + 4 l + s % 4];
+ * scale bytes of k-steps past K / 128 are zero. Run once per weight, outside the decode loop.
+ */
+int gemm_mx_pack_weight(int64_t N, int64_t K, const void *W, int64_t ldw, void *Wp, void *Sp,
+                        gemm_stream_t stream);
+
+/*
+ * gemm_mx_quantize_act: converts bf16 activations A (M x K, lda >= K, lda % 8 == 0, 16-byte
+ * aligned) to MXFP8 (E4M3) codes Aq (M x K bytes row-major, ldaq >= K, ldaq % 16 == 0, 16-byte
+ * aligned) and scales As (M x K/32 bytes, ldas >= K/32). K % 32 == 0.
+ */
+int gemm_mx_quantize_act(int64_t M, int64_t K, const void *A, int64_t lda, void *Aq, int64_t ldaq,
+                         void *As, int64_t ldas, gemm_stream_t stream);
+
+/*
+ * gemm_mx_decode: C = deq(Aq) * deq(W)^T, float32 accumulation, bf16 output (round to nearest
+ * even): C[m][n] = sum_k a[m][k] w[n][k] over the dequantised MXFP8 activations (layout of
+ * gemm_mx_quantize_act) and MXFP4 weights (packed by gemm_mx_pack_weight). C is M x N bf16
+ * (ldc >= N, ldc % 4 == 0, 8-byte aligned). Requires M <= 64, N % 16 == 0, K % 128 == 0
+ * (GEMM_ERR_UNSUPPORTED otherwise). M == 0 or N == 0: nothing; K == 0: C = 0. One launch;
+ * deterministic; shares the device workspace like the other compute calls.
+ */
+int gemm_mx_decode(int64_t M, int64_t N, int64_t K, const void *Aq, int64_t ldaq, const void *As,
+                   int64_t ldas, const void *Wp, const void *Sp, void *C, int64_t ldc,
+                   gemm_stream_t stream);
+
+/*
+ * gemm_mx_decode_bf16: gemm_mx_quantize_act into the library's workspace, then gemm_mx_decode
+ * (two launches on `stream`): the decode product from bf16 activations A (M x K, lda >= K,
+ * lda % 8 == 0, 16-byte aligned) and packed MXFP4 weights. Same requirements and results as the
+ * two calls.
+ */
+int gemm_mx_decode_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *Wp,
+                        const void *Sp, void *C, int64_t ldc, gemm_stream_t stream);
+
 /* Flags of gemm_plan_describe. */
 #define GEMM_PLAN_SKINNY 1 /* the plan of gemm_bf16_skinny */
 #define GEMM_PLAN_SWIGLU 2 /* the plan of gemm_bf16_swiglu (with GEMM_PLAN_SKINNY: its skinny form) */
+#define GEMM_PLAN_MX 4     /* the plan of gemm_mx_decode (alone) */
 
 /*
  * gemm_plan_describe: host-only. Writes, as a JSON object, the plan the library would use for an
  * M x N x K product on a device with `cus` compute units (tile, grid, schedule, split count,
  * wave count and wave efficiency = (tiles/slots)/ceil(tiles/slots), the quantity of "Kernel
- * development on sm_120", section 4, budget 4). `flags` is 0 for gemm_bf16, or a combination of
- * GEMM_PLAN_SKINNY and GEMM_PLAN_SWIGLU. Touches no HIP state. Returns GEMM_ERR_INVALID_ARG for
- * bad sizes, unknown flags or a buffer too small (buf is always NUL-terminated when len > 0),
- * GEMM_ERR_UNSUPPORTED for GEMM_PLAN_SKINNY with M outside 1 .. 64.
+ * development on sm_120", section 4, budget 4). `flags` is 0 for gemm_bf16, a combination of
+ * GEMM_PLAN_SKINNY and GEMM_PLAN_SWIGLU, or GEMM_PLAN_MX alone. Touches no HIP state. Returns
+ * GEMM_ERR_INVALID_ARG for bad sizes, unknown flags or a buffer too small (buf is always
+ * NUL-terminated when len > 0), GEMM_ERR_UNSUPPORTED for GEMM_PLAN_SKINNY with M outside 1 .. 64
+ * or GEMM_PLAN_MX outside gemm_mx_decode's shapes.
  */
 int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int flags, char *buf, int len);
 

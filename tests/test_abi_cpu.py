@@ -95,7 +95,49 @@ def test_swiglu_validation_without_gpu(args, status):
 
 def test_plan_describe_flags():
     buf = ctypes.create_string_buffer(4096)
-    assert g.lib().gemm_plan_describe(4, 64, 64, 256, 4, buf, 4096) == g.GEMM_ERR_INVALID_ARG
+    assert g.lib().gemm_plan_describe(4, 64, 64, 256, 8, buf, 4096) == g.GEMM_ERR_INVALID_ARG
+    assert g.lib().gemm_plan_describe(4, 64, 128, 256, 5, buf, 4096) == g.GEMM_ERR_INVALID_ARG
+    assert g.lib().gemm_plan_describe(4, 64, 64, 256, 4, buf, 4096) == g.GEMM_ERR_UNSUPPORTED
     assert g.lib().gemm_plan_describe(65, 64, 64, 256, 3, buf, 4096) == g.GEMM_ERR_UNSUPPORTED
     assert g.gemm_plan_describe(4, 64, 64, swiglu=True)["op"] == "swiglu"
     assert g.gemm_plan_describe(4, 64, 64)["op"] == "gemm"
+
+
+# ---- block-scaled (MX) entry points: validation on the host ---------------------------------
+
+def test_mx_packed_sizes():
+    w, s = ctypes.c_int64(), ctypes.c_int64()
+    L = g.lib()
+    assert L.gemm_mx_packed_sizes(11008, 4096, ctypes.byref(w), ctypes.byref(s)) == g.GEMM_OK
+    assert (w.value, s.value) == (688 * 32 * 1024, 688 * 8 * 256)
+    assert L.gemm_mx_packed_sizes(4096, 11008, ctypes.byref(w), ctypes.byref(s)) == g.GEMM_OK
+    assert (w.value, s.value) == (256 * 86 * 1024, 256 * 22 * 256)
+    assert L.gemm_mx_packed_sizes(17, 128, ctypes.byref(w), ctypes.byref(s)) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_mx_packed_sizes(16, 100, ctypes.byref(w), ctypes.byref(s)) == g.GEMM_ERR_INVALID_ARG
+
+
+def test_mx_validation_without_gpu():
+    L = g.lib()
+    Q = ctypes.c_void_p(4096)
+    # decode: M > 64, N % 16, K % 128 unsupported; misaligned or short leading dimensions invalid
+    assert L.gemm_mx_decode(65, 16, 128, Q, 128, Q, 4, Q, Q, Q, 16, None) == g.GEMM_ERR_UNSUPPORTED
+    assert L.gemm_mx_decode(1, 24, 128, Q, 128, Q, 4, Q, Q, Q, 24, None) == g.GEMM_ERR_UNSUPPORTED
+    assert L.gemm_mx_decode(1, 16, 96, Q, 128, Q, 4, Q, Q, Q, 16, None) == g.GEMM_ERR_UNSUPPORTED
+    assert L.gemm_mx_decode(1, 16, 128, Q, 120, Q, 4, Q, Q, Q, 16, None) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_mx_decode(1, 16, 128, Q, 136, Q, 4, Q, Q, Q, 16, None) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_mx_decode(1, 16, 128, Q, 128, Q, 3, Q, Q, Q, 16, None) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_mx_decode(1, 16, 128, Q, 128, Q, 4, Q, Q, ctypes.c_void_p(4098), 16, None) \
+        == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_mx_decode(1, 16, 128, Q, 128, Q, 4, None, Q, Q, 16, None) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_mx_decode(0, 16, 128, None, 128, None, 4, Q, Q, None, 16, None) == g.GEMM_OK
+    assert L.gemm_mx_decode(1, 16, 128, Q, 128, Q, 4, Q, Q, Q, 16, None) == g.GEMM_ERR_NOT_INITIALIZED
+    # conversions
+    assert L.gemm_mx_quantize_act(1, 48, Q, 48, Q, 48, Q, 2, None) == g.GEMM_ERR_INVALID_ARG   # K % 32
+    assert L.gemm_mx_quantize_act(1, 64, Q, 60, Q, 64, Q, 2, None) == g.GEMM_ERR_INVALID_ARG   # lda < K
+    assert L.gemm_mx_quantize_act(1, 64, Q, 64, Q, 72, Q, 2, None) == g.GEMM_ERR_INVALID_ARG   # ldaq % 16
+    assert L.gemm_mx_quantize_act(1, 64, Q, 64, Q, 64, Q, 2, None) == g.GEMM_ERR_NOT_INITIALIZED
+    assert L.gemm_mx_pack_weight(24, 128, Q, 128, Q, Q, None) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_mx_pack_weight(16, 128, Q, 120, Q, Q, None) == g.GEMM_ERR_INVALID_ARG
+    assert L.gemm_mx_pack_weight(16, 128, Q, 128, Q, Q, None) == g.GEMM_ERR_NOT_INITIALIZED
+    assert L.gemm_mx_decode_bf16(65, 16, 128, Q, 128, Q, Q, Q, 16, None) == g.GEMM_ERR_UNSUPPORTED
+    assert L.gemm_mx_decode_bf16(1, 16, 128, Q, 128, Q, Q, Q, 16, None) == g.GEMM_ERR_NOT_INITIALIZED

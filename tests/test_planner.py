@@ -157,3 +157,29 @@ def test_swiglu_skinny_plan_covers_both_halves(M):
         assert (p["strip"], p["grid"]) == (256, 172) and (q["strip"], q["grid"]) == (128, 172)
     else:
         assert p["strip"] == q["strip"] == 128 and p["grid"] == 256
+
+
+# ---- the block-scaled decode product --------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 11008, 4096), (16, 11008, 4096), (64, 11008, 4096),
+                                   (1, 4096, 11008), (64, 4096, 11008), (3, 80, 640)])
+def test_mx_plan(M, N, K):
+    p = g.gemm_plan_describe(M, N, K, mx=True)
+    assert p["kernel"] == "mx" and p["op"] == "mx"
+    tiles = N // 16
+    assert p["tiles_n"] == tiles and p["strips"] == _cdiv(tiles, 4) and p["ks"] == K // 128
+    s = p["splits"]
+    assert 1 <= s <= max(1, (K // 128) // 4)
+    assert p["grid"] == p["strips"] * s
+    # the fewest pieces whose grid covers 60% of the CUs
+    assert s == min(max(1, _cdiv(3 * 256, 5 * p["strips"])), max(1, (K // 128) // 4))
+    if (N, K) == (11008, 4096):
+        assert s == 1
+    if (N, K) == (4096, 11008):
+        assert s == 3
+
+
+def test_mx_plan_rejects_other_shapes():
+    for (M, N, K) in ((65, 4096, 4096), (1, 4100, 4096), (1, 4096, 4000)):
+        with pytest.raises(g.GemmError):
+            g.gemm_plan_describe(M, N, K, mx=True)
