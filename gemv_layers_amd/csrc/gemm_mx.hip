@@ -20,7 +20,7 @@
 //   The scales of four k-steps of a tile share 256 bytes, lane l owning byte 4 l + s % 4.
 // * mx_decode_kernel: a workgroup takes TN = 4 column tiles and one of S pieces of their k-steps;
 //   its 4 waves take contiguous quarters of the piece and run independently: no LDS and no
-//   barrier in the loop. Each wave keeps D k-steps of weights, activations and scales in flight
+//   barrier in the loop. Each wave keeps D = 2 k-steps of weights, activations and scales in flight
 //   in registers (the loads of step s + D go out as step s is consumed), and issues one scaled
 //   MFMA per tile and 16-row tile of M per k-step, with the weights as the first operand (so a
 //   lane's accumulator holds 4 consecutive columns of one row of C).
@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(const uint16_t* __restric
 // ---- the product ---------------------------------------------------------------------------------
 
 constexpr int kMxTN = 4;  // column tiles (16 columns each) per workgroup
-constexpr int kMxD = 4;   // k-steps in flight per wave
+constexpr int kMxD = 2;   // k-steps in flight per wave (measured: 2 beat 3, 4 and 6 on every decode shape)
 
 template <int MT>
 struct MxStage {

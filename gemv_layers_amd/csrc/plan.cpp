@@ -212,12 +212,12 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast
 }
 
 // Block-scaled decode: a workgroup streams the packed weights of 4 column tiles (64 columns) over
-// one of S pieces of K, its 4 waves each holding a few k-steps of loads in flight in registers.
-// Splitting K costs a float32 fixup (about 2.4 us per call on the 11008 x 4096 weight, measured),
-// so S is the smallest count whose grid covers 60% of the CUs: S = 1 for the 172 groups of an
-// 11008-wide weight (8.3 us at M = 1 against 10.7 at S = 2), S = 3 for the 64 groups of a
-// 4096-wide one (10.3 us, against 15.0 at S = 1 and 12.2 at S = 8). Every wave keeps at least one
-// k-step.
+// one of S pieces of K, its 4 waves each holding two k-steps of loads in flight in registers.
+// Splitting K costs a float32 fixup (about 2 us per call on the 11008 x 4096 weight, measured),
+// so K stays whole when one piece per group already covers 60% of the CUs (the 172 groups of an
+// 11008-wide weight: 8.3 us at M = 1 against 9.7 at S = 2) and is otherwise cut just far enough to
+// cover them all (the 64 groups of a 4096-wide weight: S = 4, 9.7 us, against 14.6 at S = 1 and
+// 10.1 at S = 3). Every wave keeps at least one k-step.
 Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     Plan p;
     p.kernel = kKernMx;
@@ -242,7 +242,7 @@ Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     p.ks = (int)(K / 128);
     const int64_t per_cu = p.mtiles <= 2 ? 2 : 1;  // waves' registers: two workgroups per CU
     p.slots = per_cu * dev.cus;
-    int64_t s = std::max<int64_t>(1, cdiv(3 * (int64_t)dev.cus, 5 * p.strips));
+    int64_t s = (5 * p.strips >= 3 * (int64_t)dev.cus) ? 1 : cdiv(dev.cus, p.strips);
     s = std::min<int64_t>(s, std::max<int64_t>(1, p.ks / 4));
     const int64_t slot_floats = (int64_t)tpg * p.mtiles * 256;
     while (s > 1 && p.strips * s * slot_floats > dev.ws_floats) --s;

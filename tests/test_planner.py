@@ -171,12 +171,13 @@ def test_mx_plan(M, N, K):
     s = p["splits"]
     assert 1 <= s <= max(1, (K // 128) // 4)
     assert p["grid"] == p["strips"] * s
-    # the fewest pieces whose grid covers 60% of the CUs
-    assert s == min(max(1, _cdiv(3 * 256, 5 * p["strips"])), max(1, (K // 128) // 4))
+    # K whole when the groups cover 60% of the CUs, else just enough pieces to cover them all
+    want = 1 if 5 * p["strips"] >= 3 * 256 else _cdiv(256, p["strips"])
+    assert s == min(want, max(1, (K // 128) // 4))
     if (N, K) == (11008, 4096):
         assert s == 1
     if (N, K) == (4096, 11008):
-        assert s == 3
+        assert s == 4
 
 
 def test_mx_plan_rejects_other_shapes():
