@@ -78,6 +78,8 @@ def parse():
                     help="skip the fused gate/up SwiGLU workloads")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the block-scaled (MXFP8 x MXFP4) decode workloads")
+    ap.add_argument("--no-packed", action="store_true",
+                    help="skip the decode workloads on packed bf16 weights")
     ap.add_argument("--swiglu-unfused-ours", action="store_true",
                     help="also time the unfused SwiGLU path on this library's own product (it runs "
                          "the plain kernels, which then also appear in a profile of this command)")
@@ -495,6 +497,80 @@ def main():
             glu[name] = rec
             del Bs, b0, Ag, Hg, Gu, Hu
         out["swiglu"] = glu
+
+    # ---------------- decode on packed bf16 weights ----------------
+    # the same products as the decode workloads, with the weight packed once into operand order
+    if not args.no_packed:
+        pkd = {}
+        copies = 12
+        packed_w = {}
+        for name in sorted(n for n in WORKLOADS if n.startswith("dec_")):
+            wd = WORKLOADS[name]
+            M, N, K = wd.M, wd.N, wd.K
+            log(f"packed {name}")
+            if (K, N) not in packed_w:
+                packed_w.clear()
+                Bh = dev(matrix("normal", K, N, seed=wd.seed_b, sigma=wd.sigma_b))
+                p0 = torch.empty(K * N, dtype=torch.bfloat16, device="cuda")
+                g.gemm_pack_weight_bf16(K, N, P(Bh), N, P(p0), sh)
+                del Bh
+                packed_w[(K, N)] = [p0] + [p0.clone() for _ in range(copies - 1)]
+            ps = packed_w[(K, N)]
+            Ad = dev(matrix("normal", M, K, seed=wd.seed_a, sigma=wd.sigma_a))
+            Cd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+            def pk_call(i):
+                g.gemm_bf16_packed(M, N, K, P(Ad), K, P(ps[i]), P(Cd), N, g.current_stream_handle())
+
+            for i in range(2 * copies):
+                pk_call(i % copies)
+            torch.cuda.synchronize()
+            e0, e1 = events(2)
+            nb = 96
+            e0.record(stream)
+            for i in range(nb):
+                pk_call(i % copies)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / nb
+            plan = g.gemm_last_plan()
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                pk_call(0)
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for i in range(copies):
+                    pk_call(i)
+            gr.replay()
+            torch.cuda.synchronize()
+            e0, e1 = events(2)
+            e0.record(stream)
+            for _ in range(8):
+                gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us_g = e0.elapsed_time(e1) * 1e3 / (8 * copies)
+            del gr
+            gbps = wd.bytes / (us * 1e-6) / 1e9
+            rec = {"us_back_to_back": round(us, 2), "us_graph_replay": round(us_g, 2),
+                   "gbps_back_to_back": round(gbps, 1),
+                   "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0,
+                                "unit": "GB/s", "frac": round(gbps / 8000.0, 4)},
+                   "tiles_per_group": plan.get("strip", 0) // 16, "splits": plan.get("splits"),
+                   "grid": plan.get("grid")}
+            if "hbm_copy_gbps" in peaks:
+                rec["frac_of_measured_copy"] = round(gbps / peaks["hbm_copy_gbps"], 4)
+            rm = out.get("decode", {}).get(name, {}).get("us_back_to_back")
+            if rm:
+                rec["row_major_us_back_to_back"] = rm
+                rec["speedup_vs_row_major"] = round(rm / us, 3)
+            pkd[name] = rec
+            del Ad, Cd
+        del packed_w
+        out["packed_decode"] = pkd
 
     # ---------------- block-scaled decode (MXFP8 activations x MXFP4 weights) ----------------
     # the decode shapes with the weight in the nn.Linear layout (N x K) packed to MXFP4 once;

@@ -26,6 +26,7 @@ GEMM_ERR_HIP = 4
 GEMM_PLAN_SKINNY = 1
 GEMM_PLAN_SWIGLU = 2
 GEMM_PLAN_MX = 4
+GEMM_PLAN_PACKED = 8
 
 # every symbol include/gemm_bf16.h declares
 EXPORTS = (
@@ -36,7 +37,7 @@ EXPORTS = (
     "gemm_peak_clock_launch",
     "gemm_peak_empty_launch", "gemm_fill_launch",
     "gemm_mx_packed_sizes", "gemm_mx_pack_weight", "gemm_mx_quantize_act", "gemm_mx_decode",
-    "gemm_mx_decode_bf16",
+    "gemm_mx_decode_bf16", "gemm_pack_weight_bf16", "gemm_bf16_packed",
 )
 
 
@@ -98,6 +99,10 @@ def lib() -> ctypes.CDLL:
     L.gemm_mx_decode.restype = i32
     L.gemm_mx_decode_bf16.argtypes = [i64, i64, i64, p, i64, p, p, p, i64, p]
     L.gemm_mx_decode_bf16.restype = i32
+    L.gemm_pack_weight_bf16.argtypes = [i64, i64, p, i64, p, p]
+    L.gemm_pack_weight_bf16.restype = i32
+    L.gemm_bf16_packed.argtypes = [i64, i64, i64, p, i64, p, p, i64, p]
+    L.gemm_bf16_packed.restype = i32
     _lib = L
     return L
 
@@ -146,10 +151,10 @@ def gemm_bf16_swiglu(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
 
 
 def gemm_plan_describe(M: int, N: int, K: int, cus: int = 256, skinny: bool = False,
-                       swiglu: bool = False, mx: bool = False) -> dict:
+                       swiglu: bool = False, mx: bool = False, packed: bool = False) -> dict:
     buf = ctypes.create_string_buffer(4096)
     flags = ((GEMM_PLAN_SKINNY if skinny else 0) | (GEMM_PLAN_SWIGLU if swiglu else 0)
-             | (GEMM_PLAN_MX if mx else 0))
+             | (GEMM_PLAN_MX if mx else 0) | (GEMM_PLAN_PACKED if packed else 0))
     _check("gemm_plan_describe", lib().gemm_plan_describe(M, N, K, cus, flags, buf, 4096))
     return json.loads(buf.value.decode())
 
@@ -175,6 +180,14 @@ def gemm_mx_decode(M, N, K, Aq, ldaq, As, ldas, Wp, Sp, C, ldc, stream=None) -> 
 
 def gemm_mx_decode_bf16(M, N, K, A, lda, Wp, Sp, C, ldc, stream=None) -> None:
     _check("gemm_mx_decode_bf16", lib().gemm_mx_decode_bf16(M, N, K, A, lda, Wp, Sp, C, ldc, stream))
+
+
+def gemm_pack_weight_bf16(K, N, B, ldb, Bp, stream=None) -> None:
+    _check("gemm_pack_weight_bf16", lib().gemm_pack_weight_bf16(K, N, B, ldb, Bp, stream))
+
+
+def gemm_bf16_packed(M, N, K, A, lda, Bp, C, ldc, stream=None) -> None:
+    _check("gemm_bf16_packed", lib().gemm_bf16_packed(M, N, K, A, lda, Bp, C, ldc, stream))
 
 
 def gemm_wave_efficiency(ctas: int, slots: int):

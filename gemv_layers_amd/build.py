@@ -15,8 +15,8 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["gemm_tile.hip", "gemm_skinny.hip", "gemm_generic.hip", "gemm_mx.hip", "peak.hip", "plan.cpp",
-           "abi.cpp"]
+SOURCES = ["gemm_tile.hip", "gemm_skinny.hip", "gemm_generic.hip", "gemm_mx.hip", "gemm_packed.hip",
+           "peak.hip", "plan.cpp", "abi.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -248,6 +248,50 @@ int mx_decode(int64_t M, int64_t N, int64_t K, const void* Aq, int64_t ldaq, con
     return GEMM_OK;
 }
 
+// ---- decode product on a packed bf16 weight ------------------------------------------------------
+
+int packed_decode(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* Bp, void* C,
+                  int64_t ldc, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldc < N) return GEMM_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && !C) return GEMM_ERR_INVALID_ARG;
+    if (M > 0 && K > 0 && !A) return GEMM_ERR_INVALID_ARG;
+    if (N > 0 && K > 0 && !Bp) return GEMM_ERR_INVALID_ARG;
+    if (M > 64 || (N % 16) || (K % 32)) return GEMM_ERR_UNSUPPORTED;
+    if (!aligned(A, 16) || !aligned(Bp, 16) || !aligned(C, 8) || (lda % 8) || (ldc % 4))
+        return GEMM_ERR_INVALID_ARG;
+    if (N * K * 2 > INT32_MAX || 64 * lda * 2 > INT32_MAX || ldc > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return GEMM_OK;
+    int st = GEMM_OK;
+    DeviceState* ds = current_state(&st);
+    if (!ds) return st;
+    const glk::Plan p = glk::make_packed_plan(M, N, K, ds->info);
+    hipError_t e = hipSuccess;
+    if (p.kernel == glk::kKernZero) {
+        e = glk::launch_zero_c(static_cast<uint16_t*>(C), M, N, ldc, stream);
+    } else {
+        glk::PkArgs a;
+        a.A = static_cast<const uint16_t*>(A);
+        a.Bp = static_cast<const uint16_t*>(Bp);
+        a.C = static_cast<uint16_t*>(C);
+        a.M = (int)M;
+        a.N = (int)N;
+        a.K = (int)K;
+        a.lda = (int)lda;
+        a.ldc = (int)ldc;
+        a.tiles = (int)(N / 16);
+        a.ks = (int)(K / 32);
+        a.pieces = p.splits;
+        a.nxcd = p.nxcd;
+        a.ws = ds->ws;
+        a.counters = ds->counters;
+        e = glk::launch_pk_decode(p.mtiles, p.strip / 16, a, (int)p.grid, stream);
+    }
+    if (e != hipSuccess) return GEMM_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_last_plan = glk::plan_json(p, M, N, K);
+    return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,6 +325,7 @@ int gemm_init(int device) {
     if (rc == GEMM_OK && glk::configure_skinny_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_tile_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_mx_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
+    if (rc == GEMM_OK && glk::configure_pk_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && hipDeviceSynchronize() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK) {
         ds.ready = true;
@@ -316,7 +361,17 @@ int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
 }
 
 int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int flags, char* buf, int len) {
-    if (M < 0 || N < 0 || K < 0 || cus <= 0 || (flags & ~7)) return GEMM_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || cus <= 0 || (flags & ~15)) return GEMM_ERR_INVALID_ARG;
+    if (flags & GEMM_PLAN_PACKED) {
+        if (flags != GEMM_PLAN_PACKED) return GEMM_ERR_INVALID_ARG;
+        if (M > 64 || (N % 16) || (K % 32)) return GEMM_ERR_UNSUPPORTED;
+        glk::DeviceInfo dev;
+        dev.cus = cus;
+        dev.nxcd = (cus % 8 == 0) ? 8 : 1;
+        dev.ws_floats = kWsFloats;
+        dev.ws_counters = kWsCounters;
+        return copy_out(glk::plan_json(glk::make_packed_plan(M, N, K, dev), M, N, K), buf, len);
+    }
     if (flags & GEMM_PLAN_MX) {
         if (flags != GEMM_PLAN_MX) return GEMM_ERR_INVALID_ARG;
         if (M > 64 || (N % 16) || (K % 128)) return GEMM_ERR_UNSUPPORTED;
@@ -434,6 +489,25 @@ int gemm_mx_decode_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
     st = mx_quantize_act(M, K, A, lda, aq, ldaq, as, ldas, s);
     if (st != GEMM_OK) return st;
     return mx_decode(M, N, K, aq, ldaq, as, ldas, Wp, Sp, C, ldc, s);
+}
+
+int gemm_pack_weight_bf16(int64_t K, int64_t N, const void* B, int64_t ldb, void* Bp, gemm_stream_t stream) {
+    if (K < 0 || N < 0 || (K % 32) || (N % 16) || ldb < N) return GEMM_ERR_INVALID_ARG;
+    if (K > 0 && N > 0 && (!B || !Bp)) return GEMM_ERR_INVALID_ARG;
+    if (!aligned(Bp, 16)) return GEMM_ERR_INVALID_ARG;
+    if (N * K * 2 > INT32_MAX || ldb > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
+    if (K == 0 || N == 0) return GEMM_OK;
+    int st = GEMM_OK;
+    if (!current_state(&st)) return st;
+    return glk::launch_pk_pack(static_cast<const uint16_t*>(B), (int)K, (int)N, (int)ldb,
+                               static_cast<uint16_t*>(Bp), reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
+int gemm_bf16_packed(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* Bp, void* C,
+                     int64_t ldc, gemm_stream_t stream) {
+    return packed_decode(M, N, K, A, lda, Bp, C, ldc, reinterpret_cast<hipStream_t>(stream));
 }
 
 int gemm_peak_mfma_launch(int64_t iters, int blocks, float* sink, uint64_t* cycles,

@@ -218,9 +218,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast
 // 11008-wide weight: 8.3 us at M = 1 against 9.7 at S = 2) and is otherwise cut just far enough to
 // cover them all (the 64 groups of a 4096-wide weight: S = 4, 9.7 us, against 14.6 at S = 1 and
 // 10.1 at S = 3). Every wave keeps at least one k-step.
-Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+// groups of `tpg` column tiles times K pieces over `ks` k-steps (see the comment above)
+static Plan decode_groups_plan(int kind, int64_t M, int64_t N, int64_t K, int64_t ks, int tpg,
+                               const DeviceInfo& dev) {
     Plan p;
-    p.kernel = kKernMx;
+    p.kernel = kind;
     if (M == 0 || N == 0) {
         p.kernel = kKernNone;
         p.reason = "empty output";
@@ -236,10 +238,9 @@ Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     p.threads = 256;
     p.mtiles = (int)cdiv(M, 16);
     p.tiles_n = N / 16;
-    const int tpg = mx_decode_tiles_per_group();
     p.strips = (int)cdiv(p.tiles_n, tpg);
     p.strip = 16 * tpg;
-    p.ks = (int)(K / 128);
+    p.ks = (int)ks;
     const int64_t per_cu = p.mtiles <= 2 ? 2 : 1;  // waves' registers: two workgroups per CU
     p.slots = per_cu * dev.cus;
     int64_t s = (5 * p.strips >= 3 * (int64_t)dev.cus) ? 1 : cdiv(dev.cus, p.strips);
@@ -252,9 +253,19 @@ Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     p.ws_floats = s > 1 ? p.strips * s * slot_floats : 0;
     p.counters = s > 1 ? p.strips : 0;
     finish_waves(p);
-    p.reason = "MXFP8 x MXFP4 decode: " + std::to_string(p.strips) + " groups of " +
-               std::to_string(tpg) + " column tiles, K in " + std::to_string(s) + " pieces";
+    p.reason = std::string(kind == kKernMx ? "MXFP8 x MXFP4 decode: " : "packed bf16 decode: ") +
+               std::to_string(p.strips) + " groups of " + std::to_string(tpg) + " column tiles, K in " +
+               std::to_string(s) + " pieces";
     return p;
+}
+
+Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+    return decode_groups_plan(kKernMx, M, N, K, K / 128, mx_decode_tiles_per_group(), dev);
+}
+
+// The packed bf16 decode reads the same kind of 1 KB operand blocks over 32-k steps.
+Plan make_packed_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+    return decode_groups_plan(kKernPacked, M, N, K, K / 32, pk_decode_tiles_per_group(M), dev);
 }
 
 static const char* kernel_name(int k) {
@@ -265,6 +276,7 @@ static const char* kernel_name(int k) {
         case kKernTile: return "tile";
         case kKernSkinny: return "skinny";
         case kKernMx: return "mx";
+        case kKernPacked: return "packed";
         default: return "?";
     }
 }
@@ -281,10 +293,13 @@ std::string plan_json(const Plan& p, int64_t M, int64_t N, int64_t K) {
              (long long)M, (long long)N, (long long)K, kernel_name(p.kernel), p.bm, p.bn, p.bk,
              p.threads, (long long)p.tiles_m, (long long)p.tiles_n, (long long)p.tiles,
              p.kernel == kKernTile ? (p.sched == kSchedSplitK ? "split-k" : "data-parallel")
-                                   : (p.kernel == kKernSkinny || p.kernel == kKernMx ? "strips" : "-"),
+                                   : (p.kernel == kKernSkinny || p.kernel == kKernMx || p.kernel == kKernPacked
+                                          ? "strips"
+                                          : "-"),
              p.splits, p.kt_per_split, p.group_m, p.nxcd, p.mtiles, p.strip, p.strips, p.ks,
              (long long)p.grid, (long long)p.slots, (long long)p.waves, p.wave_eff,
-             (long long)p.ws_floats, p.kernel == kKernMx ? "mx" : (p.glu ? "swiglu" : "gemm"),
+             (long long)p.ws_floats,
+             p.kernel == kKernMx ? "mx" : (p.kernel == kKernPacked ? "packed" : (p.glu ? "swiglu" : "gemm")),
              p.reason.c_str());
     return std::string(buf);
 }

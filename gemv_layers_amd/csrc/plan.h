@@ -9,7 +9,8 @@
 namespace glk {
 
 enum KernelKind : int {
-    kKernNone = 0, kKernZero = 1, kKernGeneric = 2, kKernTile = 3, kKernSkinny = 4, kKernMx = 5
+    kKernNone = 0, kKernZero = 1, kKernGeneric = 2, kKernTile = 3, kKernSkinny = 4, kKernMx = 5,
+    kKernPacked = 6
 };
 
 struct Plan {
@@ -64,6 +65,10 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast
 // The block-scaled decode product (1 <= M <= 64, N % 16 == 0, K % 128 == 0): groups of column
 // tiles (strips) times K pieces (splits), one workgroup each.
 Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
+
+// The decode product on a packed bf16 weight (1 <= M <= 64, N % 16 == 0, K % 32 == 0): the same
+// decomposition over 32-k steps.
+Plan make_packed_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
 
 std::string plan_json(const Plan& p, int64_t M, int64_t N, int64_t K);
 

@@ -32,7 +32,9 @@ SKINNY_SOURCES = ("gemv_layers_amd/csrc/gemm_skinny.hip", "gemv_layers_amd/csrc/
                   "gemv_layers_amd/csrc/kernels.h", "gemv_layers_amd/csrc/stream_k.h")
 MX_SOURCES = ("gemv_layers_amd/csrc/gemm_mx.hip", "gemv_layers_amd/csrc/common.h",
               "gemv_layers_amd/csrc/kernels.h")
-_SOURCES = {"tile": TILE_SOURCES, "skinny": SKINNY_SOURCES, "mx": MX_SOURCES}
+PACKED_SOURCES = ("gemv_layers_amd/csrc/gemm_packed.hip", "gemv_layers_amd/csrc/common.h",
+                  "gemv_layers_amd/csrc/kernels.h")
+_SOURCES = {"tile": TILE_SOURCES, "skinny": SKINNY_SOURCES, "mx": MX_SOURCES, "packed": PACKED_SOURCES}
 COPY_KERNEL = r"peak_copy_kernel"
 
 
@@ -140,7 +142,7 @@ def main(argv=None) -> None:
     t.add_argument("--kernel", required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--workload", required=True)
-    t.add_argument("--sources", choices=("tile", "skinny", "mx"), default="tile")
+    t.add_argument("--sources", choices=("tile", "skinny", "mx", "packed"), default="tile")
     t.add_argument("--grid", type=int, default=0, help="only dispatches with this many threads")
     t.add_argument("--algorithmic-bytes", type=int, default=0)
     t.add_argument("--command", default="")

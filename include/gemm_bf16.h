@@ -184,20 +184,50 @@ int gemm_mx_decode(int64_t M, int64_t N, int64_t K, const void *Aq, int64_t ldaq
 int gemm_mx_decode_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *Wp,
                         const void *Sp, void *C, int64_t ldc, gemm_stream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Decode on a packed bf16 weight: the decode product is a stream of weight bytes read once
+ * (spark-kernels post, "the decode kernel"); a weight that does not change between calls can be
+ * stored once in the order the matrix instructions consume it, so the product needs no staging
+ * through LDS. Same arithmetic and results contract as gemm_bf16 (bf16 in, float32 accumulation,
+ * bf16 out, round to nearest even).
+ * ------------------------------------------------------------------------------------------ */
+
+/*
+ * gemm_pack_weight_bf16: writes the K x N bf16 weight B (row-major, ldb >= N, the layout of
+ * gemm_bf16's B) into Bp (device memory of K * N * 2 bytes owned by the caller, 16-byte aligned)
+ * in the packed layout: column tile t (columns 16 t .. 16 t + 15) and k-step s (rows 32 s .. 32 s +
+ * 31) are the 1024 bytes at Bp + 1024 (t * K/32 + s); in them bytes 16 l .. 16 l + 15 (l = 0 .. 63)
+ * hold B[32 s + 8 (l / 16) + j][16 t + l % 16], j = 0 .. 7. Requires K % 32 == 0 and N % 16 == 0
+ * (GEMM_ERR_INVALID_ARG otherwise); GEMM_ERR_UNSUPPORTED beyond 2^31 - 1 bytes. Run once per weight.
+ */
+int gemm_pack_weight_bf16(int64_t K, int64_t N, const void *B, int64_t ldb, void *Bp,
+                          gemm_stream_t stream);
+
+/*
+ * gemm_bf16_packed: C = A * B for 1 <= M <= 64 with B packed by gemm_pack_weight_bf16. A is M x K
+ * bf16 (lda >= K, lda % 8 == 0, 16-byte aligned), C is M x N bf16 (ldc >= N, ldc % 4 == 0, 8-byte
+ * aligned). Requires M <= 64, N % 16 == 0, K % 32 == 0 (GEMM_ERR_UNSUPPORTED otherwise).
+ * M == 0 or N == 0: nothing; K == 0: C = 0. One launch; deterministic; shares the device
+ * workspace like the other compute calls.
+ */
+int gemm_bf16_packed(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *Bp,
+                     void *C, int64_t ldc, gemm_stream_t stream);
+
 /* Flags of gemm_plan_describe. */
 #define GEMM_PLAN_SKINNY 1 /* the plan of gemm_bf16_skinny */
 #define GEMM_PLAN_SWIGLU 2 /* the plan of gemm_bf16_swiglu (with GEMM_PLAN_SKINNY: its skinny form) */
 #define GEMM_PLAN_MX 4     /* the plan of gemm_mx_decode (alone) */
+#define GEMM_PLAN_PACKED 8 /* the plan of gemm_bf16_packed (alone) */
 
 /*
  * gemm_plan_describe: host-only. Writes, as a JSON object, the plan the library would use for an
  * M x N x K product on a device with `cus` compute units (tile, grid, schedule, split count,
  * wave count and wave efficiency = (tiles/slots)/ceil(tiles/slots), the quantity of "Kernel
  * development on sm_120", section 4, budget 4). `flags` is 0 for gemm_bf16, a combination of
- * GEMM_PLAN_SKINNY and GEMM_PLAN_SWIGLU, or GEMM_PLAN_MX alone. Touches no HIP state. Returns
+ * GEMM_PLAN_SKINNY and GEMM_PLAN_SWIGLU, or GEMM_PLAN_MX or GEMM_PLAN_PACKED alone. Touches no HIP state. Returns
  * GEMM_ERR_INVALID_ARG for bad sizes, unknown flags or a buffer too small (buf is always
  * NUL-terminated when len > 0), GEMM_ERR_UNSUPPORTED for GEMM_PLAN_SKINNY with M outside 1 .. 64
- * or GEMM_PLAN_MX outside gemm_mx_decode's shapes.
+ * or GEMM_PLAN_MX / GEMM_PLAN_PACKED outside their entry points' shapes.
  */
 int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int flags, char *buf, int len);
 

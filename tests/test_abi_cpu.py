@@ -95,7 +95,10 @@ def test_swiglu_validation_without_gpu(args, status):
 
 def test_plan_describe_flags():
     buf = ctypes.create_string_buffer(4096)
-    assert g.lib().gemm_plan_describe(4, 64, 64, 256, 8, buf, 4096) == g.GEMM_ERR_INVALID_ARG
+    assert g.lib().gemm_plan_describe(4, 64, 64, 256, 16, buf, 4096) == g.GEMM_ERR_INVALID_ARG
+    assert g.lib().gemm_plan_describe(4, 64, 64, 256, 12, buf, 4096) == g.GEMM_ERR_INVALID_ARG
+    assert g.lib().gemm_plan_describe(4, 64, 64, 256, 8, buf, 4096) == g.GEMM_OK
+    assert g.lib().gemm_plan_describe(4, 64, 48, 256, 8, buf, 4096) == g.GEMM_ERR_UNSUPPORTED
     assert g.lib().gemm_plan_describe(4, 64, 128, 256, 5, buf, 4096) == g.GEMM_ERR_INVALID_ARG
     assert g.lib().gemm_plan_describe(4, 64, 64, 256, 4, buf, 4096) == g.GEMM_ERR_UNSUPPORTED
     assert g.lib().gemm_plan_describe(65, 64, 64, 256, 3, buf, 4096) == g.GEMM_ERR_UNSUPPORTED
@@ -141,3 +144,19 @@ def test_mx_validation_without_gpu():
     assert L.gemm_mx_pack_weight(16, 128, Q, 128, Q, Q, None) == g.GEMM_ERR_NOT_INITIALIZED
     assert L.gemm_mx_decode_bf16(65, 16, 128, Q, 128, Q, Q, Q, 16, None) == g.GEMM_ERR_UNSUPPORTED
     assert L.gemm_mx_decode_bf16(1, 16, 128, Q, 128, Q, Q, Q, 16, None) == g.GEMM_ERR_NOT_INITIALIZED
+
+
+def test_packed_validation_without_gpu():
+    L = g.lib()
+    Q = ctypes.c_void_p(4096)
+    assert L.gemm_pack_weight_bf16(48, 16, Q, 16, Q, None) == g.GEMM_ERR_INVALID_ARG   # K % 32
+    assert L.gemm_pack_weight_bf16(64, 24, Q, 24, Q, None) == g.GEMM_ERR_INVALID_ARG   # N % 16
+    assert L.gemm_pack_weight_bf16(64, 16, Q, 8, Q, None) == g.GEMM_ERR_INVALID_ARG    # ldb < N
+    assert L.gemm_pack_weight_bf16(64, 16, Q, 16, Q, None) == g.GEMM_ERR_NOT_INITIALIZED
+    assert L.gemm_bf16_packed(65, 16, 64, Q, 64, Q, Q, 16, None) == g.GEMM_ERR_UNSUPPORTED
+    assert L.gemm_bf16_packed(1, 24, 64, Q, 64, Q, Q, 24, None) == g.GEMM_ERR_UNSUPPORTED
+    assert L.gemm_bf16_packed(1, 16, 48, Q, 48, Q, Q, 16, None) == g.GEMM_ERR_UNSUPPORTED
+    assert L.gemm_bf16_packed(1, 16, 64, Q, 60, Q, Q, 16, None) == g.GEMM_ERR_INVALID_ARG  # lda < K
+    assert L.gemm_bf16_packed(1, 16, 64, Q, 68, Q, Q, 16, None) == g.GEMM_ERR_INVALID_ARG  # lda % 8
+    assert L.gemm_bf16_packed(0, 16, 64, None, 64, Q, None, 16, None) == g.GEMM_OK
+    assert L.gemm_bf16_packed(1, 16, 64, Q, 64, Q, Q, 16, None) == g.GEMM_ERR_NOT_INITIALIZED
