@@ -216,3 +216,81 @@ def test_k_zero_and_determinism():
     C1, plan = run_decode(aq, as_, wp, sp, M, N, K)
     C2, _ = run_decode(aq, as_, wp, sp, M, N, K)
     assert plan["splits"] > 1 and np.array_equal(C1, C2)
+
+
+def _graph_kernel_names(graph):
+    paths = sorted({ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln})
+    hip = ctypes.CDLL(paths[0])
+    hip.hipKernelNameRefByPtr.restype = ctypes.c_char_p
+    hip.hipKernelNameRefByPtr.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    class KP(ctypes.Structure):  # hipKernelNodeParams
+        _fields_ = [("blockDim", ctypes.c_uint * 3), ("extra", ctypes.c_void_p), ("func", ctypes.c_void_p),
+                    ("gridDim", ctypes.c_uint * 3), ("kernelParams", ctypes.c_void_p),
+                    ("sharedMemBytes", ctypes.c_uint)]
+    handle = ctypes.c_void_p(graph.raw_cuda_graph())
+    n = ctypes.c_size_t(0)
+    assert hip.hipGraphGetNodes(handle, None, ctypes.byref(n)) == 0
+    nodes = (ctypes.c_void_p * max(n.value, 1))()
+    assert hip.hipGraphGetNodes(handle, nodes, ctypes.byref(n)) == 0
+    names = []
+    for i in range(n.value):
+        kind = ctypes.c_int(-1)
+        assert hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(kind)) == 0
+        assert kind.value == 0, f"node {i} is not a kernel node (type {kind.value})"
+        prm = KP()
+        assert hip.hipGraphKernelNodeGetParams(ctypes.c_void_p(nodes[i]), ctypes.byref(prm)) == 0
+        names.append((hip.hipKernelNameRefByPtr(prm.func, None) or b"").decode())
+    return names
+
+
+@pytest.mark.parametrize("entry", ["mx_decode", "mx_decode_bf16", "packed"])
+def test_graph_capture_of_decode_entry_points(entry):
+    """Captured on torch's capture stream, the calls record kernel nodes only (the conversion and
+    the product for gemm_mx_decode_bf16), run nothing during capture, and every replay equals the
+    eager result bit for bit, with other calls between replays."""
+    from oracle import packed as opk
+    M, N, K = 3, 2048, 4096
+    A, aq, as_, wq, ws, wp, sp = oracle_operands(M, N, K, 990)
+    dA = dev_bf16(A)
+    daq, das, dwp, dsp = dev_u8(np.ascontiguousarray(aq)), dev_u8(as_), dev_u8(wp), dev_u8(sp)
+    B = matrix("normal", K, N, seed=991, sigma=0.02)
+    dP = torch.from_numpy(opk.pack(B).view(np.int16)).cuda()
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        st = g.current_stream_handle()
+        if entry == "mx_decode":
+            g.gemm_mx_decode(M, N, K, P(daq), K, P(das), K // 32, P(dwp), P(dsp), P(C), N, st)
+        elif entry == "mx_decode_bf16":
+            g.gemm_mx_decode_bf16(M, N, K, P(dA), K, P(dwp), P(dsp), P(C), N, st)
+        else:
+            g.gemm_bf16_packed(M, N, K, P(dA), K, P(dP), P(C), N, st)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = C.clone()
+    g.gemm_fill_launch(P(C), C.numel() * 2, 0x7FC07FC0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph(keep_graph=True)
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    names = _graph_kernel_names(graph)
+    want = {"mx_decode": ["mx_decode_kernel"], "mx_decode_bf16": ["mx_quant_kernel", "mx_decode_kernel"],
+            "packed": ["pk_decode_kernel"]}[entry]
+    assert len(names) == len(want) and all(sum(w in n for n in names) == 1 for w in want), names
+    assert (C.view(torch.int16) == 0x7FC0).all(), "capture ran the kernels"
+    graph.instantiate()
+    other = torch.empty((2, 1024), dtype=torch.bfloat16, device="cuda")
+    for rep in range(3):
+        g.gemm_fill_launch(P(C), C.numel() * 2, 0x7FC07FC0)
+        g.gemm_bf16_packed(2, 1024, K, P(dA), K, P(dP), P(other), 1024, g.current_stream_handle())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C.view(torch.int16), eager.view(torch.int16)), f"replay {rep} of {entry}"
