@@ -198,14 +198,19 @@ int mx_quantize_act(int64_t M, int64_t K, const void* A, int64_t lda, void* Aq, 
                : GEMM_ERR_HIP;
 }
 
+// fused: A16 (bf16 activations, lda16) is converted inside the product (M <= 2), Aq/As unused
 int mx_decode(int64_t M, int64_t N, int64_t K, const void* Aq, int64_t ldaq, const void* As, int64_t ldas,
-              const void* Wp, const void* Sp, void* C, int64_t ldc, hipStream_t stream) {
+              const void* Wp, const void* Sp, void* C, int64_t ldc, hipStream_t stream,
+              const void* A16 = nullptr, int64_t lda16 = 0) {
+    const bool fused = A16 != nullptr;
     if (M < 0 || N < 0 || K < 0 || ldaq < K || ldas < K / 32 || ldc < N) return GEMM_ERR_INVALID_ARG;
     if (M > 0 && N > 0 && !C) return GEMM_ERR_INVALID_ARG;
-    if (M > 0 && K > 0 && (!Aq || !As)) return GEMM_ERR_INVALID_ARG;
+    if (!fused && M > 0 && K > 0 && (!Aq || !As)) return GEMM_ERR_INVALID_ARG;
     if (N > 0 && K > 0 && (!Wp || !Sp)) return GEMM_ERR_INVALID_ARG;
-    if (M > 64 || (N % 16) || (K % 128)) return GEMM_ERR_UNSUPPORTED;
+    if (M > 64 || (N % 16) || (K % 128) || (fused && M > 2)) return GEMM_ERR_UNSUPPORTED;
     if (!aligned(Aq, 16) || !aligned(Wp, 16) || !aligned(C, 8) || (ldaq % 16) || (ldc % 4))
+        return GEMM_ERR_INVALID_ARG;
+    if (fused && (!aligned(A16, 16) || (lda16 % 8) || lda16 < K || lda16 > INT32_MAX))
         return GEMM_ERR_INVALID_ARG;
     int64_t wb = 0, sb = 0;
     int st = mx_packed(N, K, &wb, &sb);
@@ -240,7 +245,18 @@ int mx_decode(int64_t M, int64_t N, int64_t K, const void* Aq, int64_t ldaq, con
         a.nxcd = p.nxcd;
         a.ws = ds->ws;
         a.counters = ds->counters;
-        e = glk::launch_mx_decode(p.mtiles, a, (int)p.grid, stream);
+        a.A16 = static_cast<const uint16_t*>(A16);
+        a.lda16 = (int)lda16;
+        a.kpb = 0;
+        a.red_off = 0;
+        if (fused) {
+            const int piece_ks = (a.ks + p.splits - 1) / p.splits;
+            const int lds = glk::mx_fused_layout(piece_ks, a);
+            if (lds < 0) return GEMM_ERR_UNSUPPORTED;
+            e = glk::launch_mx_decode_fused(a, (int)p.grid, lds, stream);
+        } else {
+            e = glk::launch_mx_decode(p.mtiles, a, (int)p.grid, stream);
+        }
     }
     if (e != hipSuccess) return GEMM_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_mu);
@@ -479,6 +495,19 @@ int gemm_mx_decode_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
     int st = GEMM_OK;
     DeviceState* ds = current_state(&st);
     if (!ds) return st;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    // one or two rows: converted inside the product, one launch (when the piece's rows fit LDS)
+    if (M <= 2) {
+        glk::DeviceInfo info = ds->info;
+        info.ws_floats = kMxPartialFloats;
+        const glk::Plan p = glk::make_mx_plan(M, N, K, info);
+        glk::MxArgs probe;
+        const int ks = (int)(K / 128);
+        if (p.kernel == glk::kKernMx && glk::mx_fused_layout((ks + p.splits - 1) / p.splits, probe) >= 0) {
+            // Aq/As are not read in this form; any aligned non-null pointer passes validation
+            return mx_decode(M, N, K, Wp, (K + 15) / 16 * 16, Sp, K / 32, Wp, Sp, C, ldc, hs, A, lda);
+        }
+    }
     // the quantised activations go to the workspace tail (both launches on the same stream)
     const int64_t ldaq = (K + 15) / 16 * 16, ldas = K / 32;
     if (M * ldaq + M * ldas + 16 > kMxActBytes) return GEMM_ERR_UNSUPPORTED;

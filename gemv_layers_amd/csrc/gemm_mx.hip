@@ -74,30 +74,12 @@ __device__ __forceinline__ int bf16_floor_log2(uint32_t mag) {
     return (31 - __builtin_clz(mag & 0x7Fu)) - 133;  // subnormal: m * 2^-133
 }
 
-// four consecutive lanes per (row, 32-element block), 8 elements each; the block maximum is
-// reduced across the four lanes. FP4 = false: E4M3 codes row-major into Q (ldq bytes per row) and
-// scales into S (lds bytes per row). FP4 = true: E2M1 codes and scales into the packed weight
-// layout (rows = N, a multiple of 16; cols = K, a multiple of 128); blocks past K (up to the next
-// multiple of four k-steps) get the zero scale bytes of the missing k-steps.
+// Eight elements (one lane's quarter of a 32-element block) to codes; the four lanes of a block
+// are consecutive lanes of one wave and reduce the block maximum by shuffles, so all four must
+// run this together. Returns the block's scale byte.
 template <bool FP4>
-__global__ void __launch_bounds__(256) mx_quant_kernel(const uint16_t* __restrict__ X, int rows,
-                                                       int cols, int ldx, uint8_t* __restrict__ Q,
-                                                       int ldq, uint8_t* __restrict__ S, int lds,
-                                                       int blocks_per_row) {
-    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (id >= (int64_t)rows * blocks_per_row * 4) return;  // whole groups of four lanes
-    const int64_t blk = id >> 2;
-    const int qtr = (int)(id & 3);
-    const int r = (int)(blk / blocks_per_row), b = (int)(blk - (int64_t)r * blocks_per_row);
+__device__ __forceinline__ uint8_t mx_quant8(const u32x4& v, uint32_t (&codes)[8]) {
     constexpr int EMAX = FP4 ? 2 : 8;
-    const int ks = cols / 128, kq = (ks + 3) / 4;
-    // packed position of (row, block): tile t, lane, k-step s
-    const int t = r >> 4, s = b >> 2, lane = 16 * (b & 3) + (r & 15);
-    if (b * 32 >= cols) {  // FP4 only: a k-step past K inside the last group of four
-        if (qtr == 0) S[(size_t)256 * ((size_t)t * kq + (s >> 2)) + 4 * lane + (s & 3)] = 0;
-        return;
-    }
-    const u32x4 v = *reinterpret_cast<const u32x4*>(X + (size_t)r * ldx + 32 * b + 8 * qtr);
     uint32_t amax = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -115,7 +97,6 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(const uint16_t* __restric
         se = bf16_floor_log2(amax) - EMAX;
         se = se < -127 ? -127 : (se > 127 ? 127 : se);
     }
-    uint32_t codes[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const float lo = ldexpf(bf16_lo(v[j]), -se), hi = ldexpf(bf16_hi(v[j]), -se);
@@ -127,7 +108,34 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(const uint16_t* __restric
             codes[2 * j + 1] = mx_encode<4, 3, 7>(hi, 448.0f);
         }
     }
-    const uint8_t scale = (uint8_t)(se + 127);
+    return (uint8_t)(se + 127);
+}
+
+// four consecutive lanes per (row, 32-element block), 8 elements each; the block maximum is
+// reduced across the four lanes. FP4 = false: E4M3 codes row-major into Q (ldq bytes per row) and
+// scales into S (lds bytes per row). FP4 = true: E2M1 codes and scales into the packed weight
+// layout (rows = N, a multiple of 16; cols = K, a multiple of 128); blocks past K (up to the next
+// multiple of four k-steps) get the zero scale bytes of the missing k-steps.
+template <bool FP4>
+__global__ void __launch_bounds__(256) mx_quant_kernel(const uint16_t* __restrict__ X, int rows,
+                                                       int cols, int ldx, uint8_t* __restrict__ Q,
+                                                       int ldq, uint8_t* __restrict__ S, int lds,
+                                                       int blocks_per_row) {
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= (int64_t)rows * blocks_per_row * 4) return;  // whole groups of four lanes
+    const int64_t blk = id >> 2;
+    const int qtr = (int)(id & 3);
+    const int r = (int)(blk / blocks_per_row), b = (int)(blk - (int64_t)r * blocks_per_row);
+    const int ks = cols / 128, kq = (ks + 3) / 4;
+    // packed position of (row, block): tile t, lane, k-step s
+    const int t = r >> 4, s = b >> 2, lane = 16 * (b & 3) + (r & 15);
+    if (b * 32 >= cols) {  // FP4 only: a k-step past K inside the last group of four
+        if (qtr == 0) S[(size_t)256 * ((size_t)t * kq + (s >> 2)) + 4 * lane + (s & 3)] = 0;
+        return;
+    }
+    const u32x4 v = *reinterpret_cast<const u32x4*>(X + (size_t)r * ldx + 32 * b + 8 * qtr);
+    uint32_t codes[8];
+    const uint8_t scale = mx_quant8<FP4>(v, codes);
     if (FP4) {
         uint32_t word = 0;
 #pragma unroll
@@ -145,7 +153,8 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(const uint16_t* __restric
 // ---- the product ---------------------------------------------------------------------------------
 
 constexpr int kMxTN = 4;  // column tiles (16 columns each) per workgroup
-constexpr int kMxD = 2;   // k-steps in flight per wave (measured: 2 beat 3, 4 and 6 on every decode shape)
+constexpr int kMxD = 2;
+constexpr int kMxFusedLdsMax = 160 * 1024;  // the fused form's activation rows + reduction   // k-steps in flight per wave (measured: 2 beat 3, 4 and 6 on every decode shape)
 
 template <int MT>
 struct MxStage {
@@ -155,9 +164,13 @@ struct MxStage {
     uint32_t as[MT];      // activation scale byte
 };
 
-template <int MT>
+// FUSED (M <= 2, MT = 1): the workgroup converts the bf16 activations of its K piece to MXFP8 in
+// LDS itself (while its first weight loads are in flight) and reads the activation operands from
+// there: the product from bf16 activations in one launch, with the same bits as the two-launch path.
+template <int MT, bool FUSED>
 __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
     constexpr int TN = kMxTN, D = kMxD;
+    static_assert(!FUSED || MT == 1, "the fused conversion serves one 16-row tile");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -193,6 +206,16 @@ __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
     // code 0 with scale byte 0 adds nothing)
     auto load = [&](MxStage<MT>& st, int s) {
         const bool sok = s < we;
+        if constexpr (FUSED) {  // activations come from LDS at compute time
+#pragma unroll
+            for (int t = 0; t < TN; ++t) {
+                const bool ok = sok && tile_ok[t];
+                st.w[t] = buf_load16(rw, sel_off(ok, w_base[t] + (uint32_t)s * 1024u));
+                st.ws[t] = __builtin_amdgcn_raw_buffer_load_b8(
+                    rws, sel_off(ok, ws_base[t] + (uint32_t)(s >> 2) * 256u + (uint32_t)(s & 3)), 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
             const bool ok = sok && tile_ok[t];
@@ -216,7 +239,23 @@ __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{};
 
-    auto compute = [&](const MxStage<MT>& st) {
+    // fused: activation codes [row][k - 128 pb] at lds, scales [row][block - 4 pb] at lds + 2 kpb
+    const uint8_t* aq_lds = reinterpret_cast<const uint8_t*>(lds);
+    const uint8_t* as_lds = aq_lds + 2 * p.kpb;
+    auto compute = [&](MxStage<MT>& st, int s) {
+        if constexpr (FUSED) {
+            const int m = i16, ls = s - pb;
+            u32x4 x0 = u32x4{0u, 0u, 0u, 0u}, x1 = x0;
+            uint32_t sc = 0;
+            if (m < p.M && s < we) {
+                x0 = *reinterpret_cast<const u32x4*>(aq_lds + m * p.kpb + 128 * ls + 16 * g16);
+                x1 = *reinterpret_cast<const u32x4*>(aq_lds + m * p.kpb + 128 * ls + 64 + 16 * g16);
+                sc = as_lds[m * (p.kpb / 32) + 4 * ls + g16];
+            }
+            st.a[0][0] = x0;
+            st.a[0][1] = x1;
+            st.as[0] = sc;
+        }
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
             const i32x8 wv = {(int)st.w[t][0], (int)st.w[t][1], (int)st.w[t][2], (int)st.w[t][3], 0, 0, 0, 0};
@@ -234,16 +273,34 @@ __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
     MxStage<MT> st[D];
 #pragma unroll
     for (int j = 0; j < D; ++j) load(st[j], wb + j);
+    if constexpr (FUSED) {
+        // convert rows 0 .. M-1 of A over the piece's k-steps [pb, pe) into LDS: four lanes per
+        // 32-element block (consecutive tasks of one wave), 8 elements each
+        const int nb = (pe - pb) * 4;  // blocks per row in the piece
+        const int total = p.M * nb * 4;
+        for (int task = tid; task < total; task += 256) {
+            const int m = task / (nb * 4), rem = task - m * (nb * 4);
+            const int b = rem >> 2, q = rem & 3;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(p.A16 + (size_t)m * p.lda16 + 128 * pb + 32 * b + 8 * q);
+            uint32_t codes[8];
+            const uint8_t scale = mx_quant8<false>(v, codes);
+            uint8_t* qd = reinterpret_cast<uint8_t*>(lds) + m * p.kpb + 32 * b + 8 * q;
+            *reinterpret_cast<u32x2*>(qd) = u32x2{codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24),
+                                                  codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24)};
+            if (q == 0) reinterpret_cast<uint8_t*>(lds)[2 * p.kpb + m * (p.kpb / 32) + b] = scale;
+        }
+        __syncthreads();
+    }
     for (int s0 = wb; s0 < we; s0 += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            compute(st[j]);
+            compute(st[j], s0 + j);
             load(st[j], s0 + D + j);
         }
     }
 
     // ---- the waves' sums: LDS [wave][t][mt][lane], added in wave order ----------------------
-    f32x4* red = reinterpret_cast<f32x4*>(lds);
+    f32x4* red = reinterpret_cast<f32x4*>(lds + (FUSED ? p.red_off : 0));
 #pragma unroll
     for (int t = 0; t < TN; ++t)
 #pragma unroll
@@ -289,7 +346,7 @@ __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
     }
     wait_all_memory();
     __syncthreads();
-    volatile uint32_t& last_flag = *reinterpret_cast<volatile uint32_t*>(lds);
+    volatile uint32_t& last_flag = *reinterpret_cast<volatile uint32_t*>(lds + (FUSED ? p.red_off : 0));
     if (tid == 0)
         last_flag = (counter_arrive(&p.counters[group]) == (uint32_t)(p.pieces - 1)) ? 1u : 0u;
     __syncthreads();
@@ -310,32 +367,50 @@ __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
     }
 }
 
-template <int MT>
+template <int MT, bool FUSED>
 static hipError_t mx_configure_one() {
-    return hipFuncSetAttribute((const void*)mx_decode_kernel<MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               mx_decode_lds_bytes(MT));
+    return hipFuncSetAttribute((const void*)mx_decode_kernel<MT, FUSED>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               FUSED ? kMxFusedLdsMax : mx_decode_lds_bytes(MT));
 }
 
 int mx_decode_lds_bytes(int mtiles) { return 4 * kMxTN * mtiles * 1024; }
 int mx_decode_tiles_per_group() { return kMxTN; }
 
 hipError_t configure_mx_kernels() {
-    hipError_t e = mx_configure_one<1>();
-    if (e == hipSuccess) e = mx_configure_one<2>();
-    if (e == hipSuccess) e = mx_configure_one<3>();
-    if (e == hipSuccess) e = mx_configure_one<4>();
+    hipError_t e = mx_configure_one<1, false>();
+    if (e == hipSuccess) e = mx_configure_one<2, false>();
+    if (e == hipSuccess) e = mx_configure_one<3, false>();
+    if (e == hipSuccess) e = mx_configure_one<4, false>();
+    if (e == hipSuccess) e = mx_configure_one<1, true>();
     return e;
 }
 
 hipError_t launch_mx_decode(int mtiles, const MxArgs& a, int grid, hipStream_t s) {
     const size_t lds = (size_t)mx_decode_lds_bytes(mtiles);
     switch (mtiles) {
-        case 1: mx_decode_kernel<1><<<grid, 256, lds, s>>>(a); break;
-        case 2: mx_decode_kernel<2><<<grid, 256, lds, s>>>(a); break;
-        case 3: mx_decode_kernel<3><<<grid, 256, lds, s>>>(a); break;
-        case 4: mx_decode_kernel<4><<<grid, 256, lds, s>>>(a); break;
+        case 1: mx_decode_kernel<1, false><<<grid, 256, lds, s>>>(a); break;
+        case 2: mx_decode_kernel<2, false><<<grid, 256, lds, s>>>(a); break;
+        case 3: mx_decode_kernel<3, false><<<grid, 256, lds, s>>>(a); break;
+        case 4: mx_decode_kernel<4, false><<<grid, 256, lds, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+// LDS of the fused form for pieces of at most `piece_ks` k-steps, or -1 if it does not fit; sets
+// the args' activation row stride and reduction offset
+int mx_fused_layout(int piece_ks, MxArgs& a) {
+    const int kpb = piece_ks * 128;
+    const int red_off = (2 * kpb + 2 * (kpb / 32) + 15) / 16 * 16;
+    const int bytes = red_off + mx_decode_lds_bytes(1);
+    if (bytes > kMxFusedLdsMax) return -1;
+    a.kpb = kpb;
+    a.red_off = red_off;
+    return bytes;
+}
+
+hipError_t launch_mx_decode_fused(const MxArgs& a, int grid, int lds_bytes, hipStream_t s) {
+    mx_decode_kernel<1, true><<<grid, 256, (size_t)lds_bytes, s>>>(a);
     return hipGetLastError();
 }
 

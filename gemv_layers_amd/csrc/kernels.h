@@ -94,8 +94,15 @@ struct MxArgs {
     int nxcd;            // XCDs the hardware deals workgroups over (1 = no remap)
     float* ws;           // pieces > 1: groups * pieces * 4 * mtiles * 256 floats
     uint32_t* counters;  // one per group, zero between launches
+    // the fused form (bf16 activations converted in the kernel, M <= 2): A16 (M x K bf16, lda16
+    // elements per row), LDS row stride kpb bytes and reduction offset red_off (mx_fused_layout)
+    const uint16_t* A16;
+    int lda16;
+    int kpb, red_off;
 };
 int mx_decode_tiles_per_group();
+int mx_fused_layout(int piece_ks, MxArgs& a);  // LDS bytes of the fused form, or -1
+hipError_t launch_mx_decode_fused(const MxArgs& a, int grid, int lds_bytes, hipStream_t s);
 int mx_decode_lds_bytes(int mtiles);
 hipError_t configure_mx_kernels();
 hipError_t launch_mx_decode(int mtiles, const MxArgs& a, int grid, hipStream_t s);

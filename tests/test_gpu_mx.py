@@ -294,3 +294,26 @@ def test_graph_capture_of_decode_entry_points(entry):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(C.view(torch.int16), eager.view(torch.int16)), f"replay {rep} of {entry}"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 11008, 4096), (2, 4096, 11008), (1, 80, 640), (2, 1040, 1152)])
+def test_fused_conversion_matches_two_launches(M, N, K):
+    """For one or two rows gemm_mx_decode_bf16 converts the activations inside the product (one
+    launch); its output must equal the conversion launch followed by gemm_mx_decode, bit for bit,
+    and pass the oracle's check on the oracle's own conversion."""
+    A, aq, as_, wq, ws, wp, sp = oracle_operands(M, N, K, 1500 + M)
+    dA, dwp, dsp = dev_bf16(A), dev_u8(wp), dev_u8(sp)
+    C1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    C2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    st = g.current_stream_handle()
+    g.gemm_mx_decode_bf16(M, N, K, P(dA), K, P(dwp), P(dsp), P(C1), N, st)
+    q = torch.empty(M * K, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(M * K // 32, dtype=torch.uint8, device="cuda")
+    g.gemm_mx_quantize_act(M, K, P(dA), K, P(q), K, P(sc), K // 32, st)
+    g.gemm_mx_decode(M, N, K, P(q), K, P(sc), K // 32, P(dwp), P(dsp), P(C2), N, st)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    c = C1.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref, sabs = mx.product(aq, as_, wq, ws)
+    res = oracle.check(c, ref, sabs)
+    assert res.ok, res.summary()
