@@ -208,7 +208,7 @@ int mx_decode(int64_t M, int64_t N, int64_t K, const void* Aq, int64_t ldaq, con
     if (!fused && M > 0 && K > 0 && (!Aq || !As)) return GEMM_ERR_INVALID_ARG;
     if (N > 0 && K > 0 && (!Wp || !Sp)) return GEMM_ERR_INVALID_ARG;
     if (M > 64 || (N % 16) || (K % 128) || (fused && M > 2)) return GEMM_ERR_UNSUPPORTED;
-    if (!aligned(Aq, 16) || !aligned(Wp, 16) || !aligned(C, 8) || (ldaq % 16) || (ldc % 4))
+    if ((!fused && (!aligned(Aq, 16) || (ldaq % 16))) || !aligned(Wp, 16) || !aligned(C, 8) || (ldc % 4))
         return GEMM_ERR_INVALID_ARG;
     if (fused && (!aligned(A16, 16) || (lda16 % 8) || lda16 < K || lda16 > INT32_MAX))
         return GEMM_ERR_INVALID_ARG;
@@ -504,8 +504,7 @@ int gemm_mx_decode_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
         glk::MxArgs probe;
         const int ks = (int)(K / 128);
         if (p.kernel == glk::kKernMx && glk::mx_fused_layout((ks + p.splits - 1) / p.splits, probe) >= 0) {
-            // Aq/As are not read in this form; any aligned non-null pointer passes validation
-            return mx_decode(M, N, K, Wp, (K + 15) / 16 * 16, Sp, K / 32, Wp, Sp, C, ldc, hs, A, lda);
+            return mx_decode(M, N, K, nullptr, K, nullptr, K / 32, Wp, Sp, C, ldc, hs, A, lda);
         }
     }
     // the quantised activations go to the workspace tail (both launches on the same stream)
