@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -26,7 +27,9 @@ constexpr int64_t kMxActBytes = int64_t(16) << 20;
 constexpr int64_t kMxPartialFloats = kWsFloats - kMxActBytes / 4;
 
 struct DeviceState {
-    bool ready = false;
+    // set (release) by gemm_init once the rest of the state is written; compute calls read it
+    // (acquire) without taking the lock
+    std::atomic<bool> ready{false};
     glk::DeviceInfo info;
     float* ws = nullptr;
     uint32_t* counters = nullptr;
@@ -34,7 +37,7 @@ struct DeviceState {
 
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
-int g_ready_count = 0;
+std::atomic<int> g_ready_count{0};
 std::string g_last_plan = "{}";
 
 int copy_out(const std::string& s, char* buf, int len) {
@@ -73,12 +76,14 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMM_ERR_HIP;
     DeviceState& ds = g_dev[dev];
-    if (!ds.ready) return GEMM_ERR_NOT_INITIALIZED;
+    if (!ds.ready.load(std::memory_order_acquire)) return GEMM_ERR_NOT_INITIALIZED;
 
     // (the SwiGLU form's up half starts N columns in: N % 8 == 0 keeps it 16-byte aligned)
     const bool fast = glk::fast_path_ok(M, glu ? 2 * N : N, K, A, lda, B, ldb, C, ldc) &&
                       glk::fast_path_ok(M, N, K, A, lda, B, ldb, C, ldc);
     const glk::Plan p = glk::make_plan(M, N, K, ds.info, fast, force, glu);
+    // (no buffer that fits in device memory gets here; the launch takes a 32-bit grid)
+    if (p.grid > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
     const uint16_t* a16 = static_cast<const uint16_t*>(A);
     const uint16_t* b16 = static_cast<const uint16_t*>(B);
     uint16_t* c16 = static_cast<uint16_t*>(C);
@@ -166,7 +171,7 @@ DeviceState* current_state(int* status) {
         *status = GEMM_ERR_HIP;
         return nullptr;
     }
-    if (!g_dev[dev].ready) {
+    if (!g_dev[dev].ready.load(std::memory_order_acquire)) {
         *status = GEMM_ERR_NOT_INITIALIZED;
         return nullptr;
     }
@@ -316,7 +321,7 @@ int gemm_init(int device) {
     if (device < 0 || device >= kMaxDevices) return GEMM_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lk(g_mu);
     DeviceState& ds = g_dev[device];
-    if (ds.ready) return GEMM_OK;
+    if (ds.ready.load(std::memory_order_relaxed)) return GEMM_OK;
     int count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess || device >= count) return GEMM_ERR_HIP;
     int prev = -1;
@@ -344,7 +349,7 @@ int gemm_init(int device) {
     if (rc == GEMM_OK && glk::configure_pk_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && hipDeviceSynchronize() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK) {
-        ds.ready = true;
+        ds.ready.store(true, std::memory_order_release);
         ++g_ready_count;
     } else {
         if (ds.ws) hipFree(ds.ws);
@@ -437,7 +442,7 @@ int gemm_finalize(void) {
     int rc = GEMM_OK;
     for (int d = 0; d < kMaxDevices; ++d) {
         DeviceState& ds = g_dev[d];
-        if (!ds.ready) continue;
+        if (!ds.ready.load(std::memory_order_relaxed)) continue;
         int prev = -1;
         hipGetDevice(&prev);
         hipSetDevice(d);
@@ -445,7 +450,7 @@ int gemm_finalize(void) {
         if (ds.counters && hipFree(ds.counters) != hipSuccess) rc = GEMM_ERR_HIP;
         ds.ws = nullptr;
         ds.counters = nullptr;
-        ds.ready = false;
+        ds.ready.store(false, std::memory_order_release);
         hipSetDevice(prev);
     }
     g_ready_count = 0;
