@@ -65,8 +65,11 @@ def measured_traffic(workload: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 500 steps of the 4096^3 product are about 55 ms: the card needs some 45 ms of sustained
+    # matrix-core load after an idle spell before its clock settles (per-launch time falls from
+    # about 128 to 106 us over that time), so the default warm-up covers it
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="sq4096")
     ap.add_argument("--no-peaks", action="store_true", help="skip the roof microbenchmarks")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
@@ -111,6 +114,22 @@ def main():
 
     def events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def warm(fn, ms=60.0):
+        """fn(i) back to back for about `ms` milliseconds (at least two calls), then synchronise:
+        after an idle spell (host-side input generation, a lone-launch measurement) the card takes
+        tens of milliseconds of sustained load to settle its clocks, and every timed comparison
+        below starts from that settled state."""
+        fn(0)
+        e0, e1 = events(2)
+        e0.record(stream)
+        fn(1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        n = int(ms / max(e0.elapsed_time(e1), 1e-3)) + 1
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
 
     def clock_during(launch, launch_ms, n=32):
         """Median shader clock (GHz) while `launch` runs back to back: the clock probe runs on a
@@ -248,7 +267,7 @@ def main():
     value = w.flops / (elapsed / args.steps) / 1e12
 
     # per-launch kernel duration with events on the launch stream
-    n_ev = max(10, args.steps)
+    n_ev = max(200, args.steps)
     evs = events(n_ev + 1)
     evs[0].record(stream)
     for i in range(n_ev):
@@ -303,15 +322,14 @@ def main():
     try:
         if args.no_torch:
             raise RuntimeError("skipped (--no-torch)")
-        for _ in range(5):
-            torch.matmul(A, B)
+        warm(lambda i: torch.matmul(A, B))
         e0, e1 = events(2)
         e0.record(stream)
-        for _ in range(20):
+        for _ in range(200):
             torch.matmul(A, B)
         e1.record(stream)
         torch.cuda.synchronize()
-        headline["torch_matmul_tflops"] = round(w.flops / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12, 1)
+        headline["torch_matmul_tflops"] = round(w.flops / (e0.elapsed_time(e1) / 200 * 1e-3) / 1e12, 1)
     except Exception as exc:  # comparison arm only
         headline["torch_matmul_error"] = str(exc)[:200]
     out["headline"] = headline
@@ -336,9 +354,7 @@ def main():
             def call(b):
                 g.gemm_bf16(wd.M, wd.N, wd.K, P(Ad), wd.K, P(b), wd.N, P(Cd), wd.N, sh)
 
-            for i in range(2 * copies):
-                call(Bs[i % copies])
-            torch.cuda.synchronize()
+            warm(lambda i: call(Bs[i % copies]))
             singles = []
             for i in range(48):
                 e0, e1 = events(2)
@@ -348,6 +364,7 @@ def main():
                 torch.cuda.synchronize()
                 singles.append(e0.elapsed_time(e1) * 1e3)
             nb = 96
+            warm(lambda i: call(Bs[i % copies]), ms=20.0)  # (after the lone launches' idle gaps)
             e0, e1 = events(2)
             e0.record(stream)
             for i in range(nb):
@@ -450,9 +467,7 @@ def main():
 
             def per_call_us(fn, n, rounds=3):
                 """Mean per call of n calls back to back between two events, per round."""
-                for i in range(2 * copies):
-                    fn(Bs[i % copies])
-                torch.cuda.synchronize()
+                warm(lambda i: fn(Bs[i % copies]))
                 res = []
                 for _ in range(rounds):
                     e0, e1 = events(2)
@@ -522,9 +537,7 @@ def main():
             def pk_call(i):
                 g.gemm_bf16_packed(M, N, K, P(Ad), K, P(ps[i]), P(Cd), N, g.current_stream_handle())
 
-            for i in range(2 * copies):
-                pk_call(i % copies)
-            torch.cuda.synchronize()
+            warm(lambda i: pk_call(i % copies))
             e0, e1 = events(2)
             nb = 96
             e0.record(stream)
@@ -602,9 +615,7 @@ def main():
             Cd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
             def b2b_us(fn, n=160):
-                for i in range(2 * copies):
-                    fn(i % copies)
-                torch.cuda.synchronize()
+                warm(lambda i: fn(i % copies))
                 e0, e1 = events(2)
                 e0.record(stream)
                 for i in range(n):
@@ -682,8 +693,7 @@ def main():
             Bl = dev(matrix("normal", wl.K, wl.N, seed=wl.seed_b, sigma=wl.sigma_b))
             Cl = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
             n = 20 if wl.flops < 2e12 else 5
-            for _ in range(3):
-                g.gemm_bf16(wl.M, wl.N, wl.K, P(Al), wl.K, P(Bl), wl.N, P(Cl), wl.N, sh)
+            warm(lambda i: g.gemm_bf16(wl.M, wl.N, wl.K, P(Al), wl.K, P(Bl), wl.N, P(Cl), wl.N, sh))
             evl = events(n + 1)
             evl[0].record(stream)
             for i in range(n):
