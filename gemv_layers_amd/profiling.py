@@ -5,8 +5,15 @@
         --write <counter_collection.csv> --kernel REGEX --copy-bytes N --workload NAME
         [--algorithmic-bytes B] [--command CMD]
 
+    python -m gemv_layers_amd.profiling window <run_kernel_trace.csv> --kernel REGEX --skip N
+        --count K [--grid THREADS]
+
 `stats` prints the per-kernel table of a `--kernel-trace --stats --output-format csv` run (the
 kernels matching REGEX only, when given).
+`window` takes the dispatches of the matching kernel in dispatch order, skips the first N and
+prints the mean, minimum and maximum duration of the next K, and their span (first start to
+last end) divided by K: e.g. the timed region of a benchmark that runs N warm-up launches
+first.
 `traffic` turns two counter passes (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, both over a
 command that also runs the library's copy kernel on `--copy-bytes` bytes, e.g.
 `bench.py --copy-calibration`) into HBM bytes per launch of the kernel matching REGEX: each
@@ -91,6 +98,27 @@ def cmd_stats(a) -> None:
               f"{r['max_ns'] / 1e3:10.3f} {r['percent']:7.3f}  {name}")
 
 
+def cmd_window(a) -> None:
+    rx = re.compile(a.kernel)
+    rows = []
+    with open(a.csv, newline="") as f:
+        for r in csv.DictReader(f):
+            if rx.search(r["Kernel_Name"]) and (not a.grid or int(r["Grid_Size_X"]) == a.grid):
+                rows.append((int(r["Dispatch_Id"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    win = rows[a.skip:a.skip + a.count]
+    if len(win) < a.count:
+        raise SystemExit(f"only {len(rows)} matching dispatches")
+    durs = [(e - b) / 1e3 for _, b, e in win]
+    span = (win[-1][2] - win[0][1]) / 1e3
+    print(f"# dispatches {a.skip} .. {a.skip + a.count - 1} of the kernel matching /{a.kernel}/"
+          + (f", grid {a.grid} threads" if a.grid else "") + f" ({len(rows)} in the trace)")
+    print(f"mean_us: {sum(durs) / len(durs):.3f}")
+    print(f"min_us: {min(durs):.3f}")
+    print(f"max_us: {max(durs):.3f}")
+    print(f"span_over_count_us: {span / a.count:.3f}")
+
+
 def cmd_traffic(a) -> None:
     kib = 1024.0
     f_copy = _mean(counter_per_dispatch(a.fetch, "FETCH_SIZE", COPY_KERNEL))
@@ -146,8 +174,14 @@ def main(argv=None) -> None:
     t.add_argument("--grid", type=int, default=0, help="only dispatches with this many threads")
     t.add_argument("--algorithmic-bytes", type=int, default=0)
     t.add_argument("--command", default="")
+    w = sub.add_parser("window")
+    w.add_argument("csv")
+    w.add_argument("--kernel", required=True)
+    w.add_argument("--skip", type=int, default=0)
+    w.add_argument("--count", type=int, required=True)
+    w.add_argument("--grid", type=int, default=0, help="only dispatches with this many threads")
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "window": cmd_window}[a.cmd](a)
 
 
 if __name__ == "__main__":
