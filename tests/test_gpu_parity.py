@@ -222,8 +222,8 @@ def test_epilogue_rounds_to_nearest_even(entry, M):
     for j in range(N):
         x, bits = ties[j % len(ties)]
         sgn = -1.0 if x < 0 else 1.0
-        B[0, j] = oracle.bf16_rne(sgn * 4096.0)
-        B[1, j] = oracle.bf16_rne(x - sgn * 4096.0)
+        B[0, j] = oracle.bf16_rne(sgn * 4096.0)[0]
+        B[1, j] = oracle.bf16_rne(x - sgn * 4096.0)[0]
         want[j] = bits
     C = run(entry, A, B, M, N, K)
     assert np.all(C == want[None, :])
