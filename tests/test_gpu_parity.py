@@ -175,6 +175,20 @@ def test_leading_dimensions_never_read_padding(entry):
     assert oracle.check(C, ref, sabs).ok
 
 
+@pytest.mark.parametrize("entry,M,ld_extra,kernel", [("tiled", 256, 0, "tile"), ("skinny", 64, 0, "skinny"),
+                                                     ("auto", 256, 8, "generic")])
+def test_largest_leading_dimensions(entry, M, ld_extra, kernel):
+    # the fast kernels take leading dimensions up to 2^20 elements (32-bit buffer offsets over
+    # a tile's rows); one more 16-byte unit sends the call to the general kernel
+    LD = (1 << 20) + ld_extra
+    N, K = 136, 72
+    A = matrix("normal", M, K, seed=21, ld=LD)
+    B = matrix("normal", K, N, seed=22, ld=LD)
+    C = run(entry, A, B, M, N, K, ldc=LD)
+    assert g.gemm_last_plan()["kernel"] == kernel
+    check_float(C, A, B, M, N, K, f"{entry} ld={LD}")
+
+
 def test_dispatch_on_m():
     A64, A65 = matrix("int", 64, 512, seed=1), matrix("int", 65, 512, seed=1)
     B = matrix("int", 512, 1024, seed=2)
