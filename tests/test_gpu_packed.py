@@ -113,3 +113,38 @@ def test_ldc_padding_k_zero_and_determinism():
     assert oracle.check(C1[:, :N], ref, sabs).ok
     C0, _ = run_packed(np.zeros((2, 0), np.uint16), np.zeros((0, 32), np.uint16), 2, 32, 0)
     assert (C0 == 0).all()
+
+
+def test_largest_packed_weight_and_row_major_stream():
+    # the largest weight gemm_bf16_packed takes (2 K N bytes just under 2^31: 32-bit offsets),
+    # with a 0/1 weight whose pattern differs from column to column, (k + 3 n) % 7 == 0, and
+    # integer activations: every partial sum is an integer below 2^24, so the result is exact and
+    # C[m][n] is the bf16 rounding of the sum of A[m][k] over k = -3 n (mod 7). The same weight
+    # also goes through the row-major entry (gemm_bf16, M <= 64: the skinny kernel).
+    M, K, N = 2, 32768, 32752
+    assert 2 * K * N <= 2**31 - 1
+    A = matrix("int", M, K, seed=1500, radius=2)
+    kk = torch.arange(K, device="cuda", dtype=torch.int32)[:, None]
+    nn = torch.arange(N, device="cuda", dtype=torch.int32)[None, :]
+    B = ((kk + 3 * nn) % 7 == 0).to(torch.bfloat16)
+    del kk, nn
+    s = g.current_stream_handle()
+    Bp = torch.empty(K * N, dtype=torch.bfloat16, device="cuda")
+    g.gemm_pack_weight_bf16(K, N, P(B), N, P(Bp), s)
+    dA = dev16(A)
+    Af = oracle.bf16_to_f64(A)
+    residue = np.arange(K) % 7
+    sums = np.stack([Af[:, residue == c].sum(axis=1) for c in range(7)], axis=1)  # M x 7, exact
+    want = oracle.bf16_rne(sums[:, (-3 * np.arange(N)) % 7])
+    for name in ("packed", "row-major"):
+        C = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        if name == "packed":
+            g.gemm_bf16_packed(M, N, K, P(dA), K, P(Bp), P(C), N, s)
+        else:
+            g.gemm_bf16(M, N, K, P(dA), K, P(B), N, P(C), N, s)
+        torch.cuda.synchronize()
+        got = C.cpu().view(torch.int16).numpy().view(np.uint16)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"{name}: {len(bad)} mismatches, first at {bad[0].tolist()}"
+    del B, Bp
+    torch.cuda.empty_cache()
