@@ -317,3 +317,41 @@ def test_fused_conversion_matches_two_launches(M, N, K):
     ref, sabs = mx.product(aq, as_, wq, ws)
     res = oracle.check(c, ref, sabs)
     assert res.ok, res.summary()
+
+
+def test_largest_packed_mx_weight():
+    # the largest weight the MX entries take: N K / 2 code bytes just under 2^31 (32-bit offsets).
+    # W[n][k] = 1 where (k + 3 n) % 7 == 0, else 0 (nn.Linear layout, N x K), and integer
+    # activations in [-2, 2]: both convert exactly (a weight block holding a 1 gets scale 2^-2 and
+    # code 4.0; an activation block with maximum 2 gets scale 2^-7 and codes 0, +-128, +-256, with
+    # maximum 1 scale 2^-8), every product and partial sum is an integer below 2^24, so C[m][n]
+    # is the bf16 rounding of the sum of A[m][k] over k = -3 n (mod 7). Through
+    # gemm_mx_decode_bf16 at M = 2 (the conversion inside the product).
+    M, N, K = 2, 65520, 65536
+    wb, sb = g.gemm_mx_packed_sizes(N, K)
+    assert wb <= 2**31 - 1 and wb == N * K // 2
+    A = matrix("int", M, K, seed=1600, radius=2)
+    W = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    kk = torch.arange(K, device="cuda", dtype=torch.int32)[None, :]
+    for r0 in range(0, N, 2048):
+        nn = torch.arange(r0, min(N, r0 + 2048), device="cuda", dtype=torch.int32)[:, None]
+        W[r0:r0 + nn.shape[0]] = ((kk + 3 * nn) % 7 == 0).to(torch.bfloat16)
+    del kk, nn
+    s = g.current_stream_handle()
+    wp = torch.empty(wb, dtype=torch.uint8, device="cuda")
+    sp = torch.empty(sb, dtype=torch.uint8, device="cuda")
+    g.gemm_mx_pack_weight(N, K, P(W), K, P(wp), P(sp), s)
+    del W
+    dA = dev_bf16(A)
+    C = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    g.gemm_mx_decode_bf16(M, N, K, P(dA), K, P(wp), P(sp), P(C), N, s)
+    torch.cuda.synchronize()
+    Af = oracle.bf16_to_f64(A)
+    residue = np.arange(K) % 7
+    sums = np.stack([Af[:, residue == c].sum(axis=1) for c in range(7)], axis=1)  # M x 7, exact
+    want = oracle.bf16_rne(sums[:, (-3 * np.arange(N)) % 7])
+    got = C.cpu().view(torch.int16).numpy().view(np.uint16)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[0].tolist()}"
+    del wp, sp
+    torch.cuda.empty_cache()
