@@ -317,17 +317,38 @@ tile_gemm_kernel(TileArgs p) {
             __syncthreads();
             if (!last_flag) return;
             if (tid == 0) counter_reset(&p.counters[tile]);
-            // sum the pieces in K order: piece 0 first
+            // sum the pieces in K order, piece 0 first, with all of a piece's loads in flight
+            // before its adds (one memory latency per piece, not one per fragment)
+            f32x4 sum[TN][TM];
 #pragma unroll
             for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-                for (int mi = 0; mi < TM; ++mi) {
-                    const uint32_t off = (uint32_t)((((wave * TN + ni) * TM + mi) * 64 + lane) * 16);
-                    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-                    for (int pc = 0; pc < npieces; ++pc)
-                        s += (pc == piece) ? acc[ni][mi] : bits_f4(buf_load16_dev(ws, (uint32_t)pc * slot_bytes + off));
-                    acc[ni][mi] = s;
+                for (int mi = 0; mi < TM; ++mi) sum[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int pc = 0; pc < npieces; ++pc) {
+                if (pc == piece) {
+#pragma unroll
+                    for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                        for (int mi = 0; mi < TM; ++mi) sum[ni][mi] += acc[ni][mi];
+                    continue;
                 }
+                f32x4 v[TN][TM];
+#pragma unroll
+                for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                    for (int mi = 0; mi < TM; ++mi) {
+                        const uint32_t off = (uint32_t)((((wave * TN + ni) * TM + mi) * 64 + lane) * 16);
+                        v[ni][mi] = bits_f4(buf_load16_dev(ws, (uint32_t)pc * slot_bytes + off));
+                    }
+#pragma unroll
+                for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                    for (int mi = 0; mi < TM; ++mi) sum[ni][mi] += v[ni][mi];
+            }
+#pragma unroll
+            for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < TM; ++mi) acc[ni][mi] = sum[ni][mi];
         }
     }
 

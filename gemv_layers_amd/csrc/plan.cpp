@@ -151,11 +151,16 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     p.slots = (int64_t)dev.cus * per_cu;
     // only the smaller tiles carry the split fixup
     if (p.tiles < p.slots && kt_total > 1 && p.tile_cfg == kTile128x128w4) {
-        // split K over the idle slots; pieces are summed in K order by the last arriver. Each
-        // piece keeps at least kMinPieceSteps k-steps: the last arriver reads every other piece's
-        // float32 tile (BM*BN*4 bytes each), which costs more than a few k-steps of MFMA work.
-        constexpr int64_t kMinPieceSteps = 8;
-        int64_t s = std::min<int64_t>(kt_total / kMinPieceSteps, std::max<int64_t>(1, p.slots / p.tiles));
+        // split K over the idle CUs; pieces are summed in K order by the last arriver, which
+        // reads every other piece's float32 tile (BM*BN*4 bytes), one memory round trip per piece
+        // (about 1.2 us), against about 0.4 us per k-step of a lone 128x128 workgroup. So the
+        // pieces number about sqrt(kt / 3), and at most one workgroup per CU: two co-resident
+        // pieces of different tiles ran slower than one unsplit tile (measured, settled clocks:
+        // 2048^3 unsplit 30 us against 42 us in 2 pieces per tile; 1024 x 1024 x 8192 in 4 pieces
+        // 35 us against 50 us in 8; 128 x 128 x 65536 in 32 pieces 48 us against 160 us in 256).
+        int64_t root = 1;
+        while ((root + 1) * (root + 1) * 3 <= kt_total) ++root;
+        int64_t s = std::min<int64_t>(root, std::max<int64_t>(1, dev.cus / p.tiles));
         s = std::max<int64_t>(s, 1);
         const int64_t slot_floats = (int64_t)p.bm * p.bn;
         while (s > 1 && p.tiles * s * slot_floats > dev.ws_floats) --s;

@@ -69,17 +69,26 @@ def test_small_square_splits_k():
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 512, 512), (1000, 1000, 1000), (257, 264, 4104),
-                                   (300, 520, 328), (128, 128, 96), (200, 2000, 20000)])
-def test_split_pieces_keep_eight_k_steps(M, N, K):
-    # the last arriver reads every other piece's float32 tile, so a piece must carry at least
-    # eight k-steps of MFMA work; shapes with fewer k-steps in all are not split
+                                   (300, 520, 328), (128, 128, 96), (200, 2000, 20000),
+                                   (2048, 2048, 2048), (1024, 1024, 8192), (128, 128, 65536),
+                                   (2048, 1024, 4096)])
+def test_split_count_follows_the_measured_rule(M, N, K):
+    # each piece costs the last arriver one memory round trip, about three k-steps of a lone
+    # workgroup, so K is cut into about sqrt(kt / 3) pieces, and into no more pieces than leave
+    # one workgroup per CU; no piece is empty
     p = g.gemm_plan_describe(M, N, K, 256)
     kt = -(-K // p["bk"])
-    if p["schedule"] == "split-k":
-        assert p["kt_per_split"] >= 8 and p["splits"] >= 2
+    root = 1
+    while 3 * (root + 1) ** 2 <= kt:
+        root += 1
+    want = max(1, min(root, 256 // p["tiles"])) if p["bm"] == 128 else 1
+    if want > 1:
+        per = -(-kt // want)
+        assert p["schedule"] == "split-k" and p["kt_per_split"] == per and p["splits"] == -(-kt // per)
         assert (p["splits"] - 1) * p["kt_per_split"] < kt <= p["splits"] * p["kt_per_split"]
+        assert p["grid"] == p["tiles"] * p["splits"] <= 256
     else:
-        assert p["splits"] == 1 and (kt < 16 or p["tiles"] >= p["slots"])
+        assert p["splits"] == 1 and p["schedule"] == "data-parallel"
 
 
 @pytest.mark.parametrize("name", [n for n in WORKLOADS if n.startswith("dec_")])
