@@ -170,11 +170,20 @@ __global__ void __launch_bounds__(256) pk_decode_kernel(PkArgs p) {
         const int j = 4 * q + wave;
         if (j >= NJ) continue;
         const bool ok = 16 * (j % MT) + i16 < p.M;
+        // in K order, four pieces' loads in flight before their adds
         f32x4 x = f32x4{};
-        for (int pc = 0; pc < p.pieces; ++pc)
-            x += (pc == piece) ? sum[q]
-                               : bits_f4(buf_load16_dev(rws, sel_off(ok, first + (uint32_t)pc * slot +
-                                                                             (uint32_t)j * 1024u + 16u * lane)));
+        for (int b0 = 0; b0 < p.pieces; b0 += 4) {
+            f32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int pc = b0 + u;
+                const bool ld = ok && pc < p.pieces && pc != piece;
+                v[u] = bits_f4(buf_load16_dev(rws, sel_off(ld, first + (uint32_t)pc * slot + (uint32_t)j * 1024u + 16u * lane)));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (b0 + u < p.pieces) x += (b0 + u == piece) ? sum[q] : v[u];
+        }
         store_c(j, x);
     }
 }
