@@ -131,11 +131,18 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     p.kernel = kKernTile;
     p.nxcd = dev.nxcd;
     set_tile(p, kTile256x256w8, M, N);
+    // A wave of 256x256 tiles takes about as long as a wave of 128x128 tiles at two per CU while
+    // doing twice the work, and a partial wave of them runs faster per tile, so the big tile wins
+    // down to about 5/16 of the CUs busy (measured, settled clocks: 86 tiles 90 us against 99 us
+    // as 344 small ones at 512 x 11008 x 4096; 172 tiles 91 against 148 us at 1024 x 11008 x 4096;
+    // 64 tiles 50 against 28 us at 2048^3, where the small tiles fill the card).
     if (p.tiles >= dev.cus) {
         p.reason = "256x256 tiles fill at least one wave";
+    } else if (16 * p.tiles >= 5 * (int64_t)dev.cus) {
+        p.reason = "256x256 tiles occupy at least 5/16 of the CUs";
     } else {
         set_tile(p, kTile128x128w4, M, N);
-        p.reason = "256x256 grid below one wave: 128x128 tiles";
+        p.reason = "256x256 grid below 5/16 of the CUs: 128x128 tiles";
     }
     if (dev.force_tile_cfg >= 0 && dev.force_tile_cfg < kTileConfigCount) {
         set_tile(p, dev.force_tile_cfg, M, N);

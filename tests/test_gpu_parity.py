@@ -78,7 +78,9 @@ def check_exact(C, A, B, M, N, K, what=""):
 # ---- small and ragged shapes, each kernel family --------------------------------------------
 
 TILE_SHAPES = [(256, 256, 64), (512, 512, 512), (300, 520, 328), (1000, 1000, 1000),
-               (65, 264, 72), (1, 8, 8), (257, 264, 4104), (513, 1032, 136)]
+               (65, 264, 72), (1, 8, 8), (257, 264, 4104), (513, 1032, 136),
+               # 256 x 256 tiles in a partial wave (80 and 108 tiles), ragged in M, N and K
+               (1000, 5000, 328), (777, 6704, 200)]
 
 
 @pytest.mark.parametrize("M,N,K", TILE_SHAPES)
@@ -89,6 +91,8 @@ def test_tile_kernel_float_and_exact(M, N, K):
     Ai = matrix("int", M, K, seed=3000 + M)
     Bi = matrix("int", K, N, seed=4000 + N)
     check_exact(run("tiled", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"tiled int {M}x{N}x{K}")
+    if 16 * (-(-M // 256)) * (-(-N // 256)) >= 5 * 256:
+        assert g.gemm_last_plan()["bm"] == 256
 
 
 SKINNY_SHAPES = [(m, n, k) for m in (1, 2, 3, 16, 17, 33, 64)
