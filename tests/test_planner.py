@@ -193,3 +193,15 @@ def test_mx_plan_rejects_other_shapes():
     for (M, N, K) in ((65, 4096, 4096), (1, 4100, 4096), (1, 4096, 4000)):
         with pytest.raises(g.GemmError):
             g.gemm_plan_describe(M, N, K, mx=True)
+
+
+@pytest.mark.parametrize("M,N,K,bm", [(1024, 11008, 4096, 256), (512, 11008, 4096, 256), (3072, 4096, 4096, 256),
+                                      (2048, 2048, 2048, 128), (1024, 4096, 11008, 128),
+                                      (256, 80 * 256, 1024, 256), (256, 79 * 256, 1024, 128)])
+def test_big_tiles_down_to_five_sixteenths_of_the_cus(M, N, K, bm):
+    # a wave of 256 x 256 tiles does twice the work of a wave of 128 x 128 tiles at two per CU in
+    # about the same time, so the big tiles are kept while they occupy at least 5/16 of the CUs
+    p = g.gemm_plan_describe(M, N, K, 256)
+    assert p["kernel"] == "tile" and p["bm"] == bm, p
+    if bm == 256:
+        assert p["splits"] == 1 and p["schedule"] == "data-parallel"
