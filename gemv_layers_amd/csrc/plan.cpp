@@ -131,18 +131,19 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     p.kernel = kKernTile;
     p.nxcd = dev.nxcd;
     set_tile(p, kTile256x256w8, M, N);
-    // A wave of 256x256 tiles takes about as long as a wave of 128x128 tiles at two per CU while
-    // doing twice the work, and a partial wave of them runs faster per tile, so the big tile wins
-    // down to about 5/16 of the CUs busy (measured, settled clocks: 86 tiles 90 us against 99 us
-    // as 344 small ones at 512 x 11008 x 4096; 172 tiles 91 against 148 us at 1024 x 11008 x 4096;
-    // 64 tiles 50 against 28 us at 2048^3, where the small tiles fill the card).
+    // A 128x128 tile takes about half as long as a 256x256 one (51 against 90 us at K = 4096 in a
+    // partial wave), but a second 128x128 workgroup on a CU does not overlap the first: a grid of
+    // more small tiles than CUs takes two of their waves (99 us for 272 to 336 tiles). So the
+    // small tiles serve only grids they cover in one wave (measured, settled clocks: 2048^3 as
+    // 256 small tiles 28 us against 50 us as 64 big ones; 1024 x 4352 x 4096 as 68 big tiles
+    // 90 us against 99 us as 272 small ones).
     if (p.tiles >= dev.cus) {
         p.reason = "256x256 tiles fill at least one wave";
-    } else if (16 * p.tiles >= 5 * (int64_t)dev.cus) {
-        p.reason = "256x256 tiles occupy at least 5/16 of the CUs";
+    } else if (cdiv(M, tile_shape(kTile128x128w4).bm) * cdiv(N, tile_shape(kTile128x128w4).bn) > dev.cus) {
+        p.reason = "128x128 tiles would need a second wave: 256x256 tiles";
     } else {
         set_tile(p, kTile128x128w4, M, N);
-        p.reason = "256x256 grid below 5/16 of the CUs: 128x128 tiles";
+        p.reason = "128x128 tiles in one wave";
     }
     if (dev.force_tile_cfg >= 0 && dev.force_tile_cfg < kTileConfigCount) {
         set_tile(p, dev.force_tile_cfg, M, N);
@@ -153,9 +154,9 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     p.sched = kSchedDataParallel;
     p.splits = 1;
     p.kt_per_split = (int)kt_total;
-    // 256-wide tiles take 128 KB of LDS (one workgroup per CU); 128x128 tiles take 64 KB
-    const int per_cu = (p.tile_cfg == kTile128x128w4) ? 2 : 1;
-    p.slots = (int64_t)dev.cus * per_cu;
+    // one workgroup per CU at a time: the 256-wide tile takes all of LDS, and a second 128x128
+    // workgroup on a CU does not overlap the first (measured)
+    p.slots = (int64_t)dev.cus;
     // only the smaller tiles carry the split fixup
     if (p.tiles < p.slots && kt_total > 1 && p.tile_cfg == kTile128x128w4) {
         // split K over the idle CUs; pieces are summed in K order by the last arriver, which

@@ -197,11 +197,14 @@ def test_mx_plan_rejects_other_shapes():
 
 @pytest.mark.parametrize("M,N,K,bm", [(1024, 11008, 4096, 256), (512, 11008, 4096, 256), (3072, 4096, 4096, 256),
                                       (2048, 2048, 2048, 128), (1024, 4096, 11008, 128),
-                                      (256, 80 * 256, 1024, 256), (256, 79 * 256, 1024, 128)])
-def test_big_tiles_down_to_five_sixteenths_of_the_cus(M, N, K, bm):
-    # a wave of 256 x 256 tiles does twice the work of a wave of 128 x 128 tiles at two per CU in
-    # about the same time, so the big tiles are kept while they occupy at least 5/16 of the CUs
+                                      (1024, 4352, 4096, 256), (1024, 4096, 4096, 128),
+                                      (1000, 4104, 512, 256), (1000, 4096, 512, 128)])
+def test_small_tiles_only_in_one_wave(M, N, K, bm):
+    # a second 128 x 128 workgroup on a CU does not overlap the first, so 128 x 128 tiles serve
+    # only grids they cover in one wave; otherwise 256 x 256 tiles, in a partial wave if need be
     p = g.gemm_plan_describe(M, N, K, 256)
     assert p["kernel"] == "tile" and p["bm"] == bm, p
+    small = -(-M // 128) * -(-N // 128)
+    assert (small <= 256) == (bm == 128)
     if bm == 256:
         assert p["splits"] == 1 and p["schedule"] == "data-parallel"
