@@ -12,8 +12,8 @@
 //   (group_m tile rows at a time), so the tiles resident on one XCD share A rows and B columns
 //   in that XCD's L2.
 // * K advances in steps of BK = 32. A and B are copied HBM -> LDS by direct-to-LDS buffer loads
-//   (1 KB per wave instruction, no registers) into two rings that together fill LDS: B in stages of
-//   32 x BN, A in stages of BM x 64 so that every A row the loads touch is one whole 128-byte
+//   (1 KB per wave instruction, no registers) into two rings: B in 3 stages of 32 x BN, A in 3
+//   stages of BM x 64 so that every A row the loads touch is one whole 128-byte
 //   line (32-k stages would fetch half lines, which costs the address unit about a third more per
 //   byte). Each step every wave issues the same loads: half an A stage and one B stage, several
 //   steps ahead of use; one barrier per step, with no memory fence, so later loads stay in flight.
@@ -53,11 +53,11 @@ template <int BM, int BN, int WM, int WN>
 struct TileTraits {
     static constexpr int BK = 32;                           // k per step (B stage, MFMA step)
     static constexpr int AK = 64;                           // k per A stage: 128-byte rows
-    // A ring SA stages of BM x 64, B ring SB stages of 32 x BN: all 160 KB of LDS for the
-    // 256 x 256 tile; for 128 x 128 tiles a 3-stage B ring (72 KB in all), which measured about
-    // 10% faster than 4 stages (80 KB) on every small-tile grid, with the same bits
+    // A ring SA stages of BM x 64, B ring SB stages of 32 x BN (144 KB for the 256 x 256 tile,
+    // 72 KB for 128 x 128). A 3-stage B ring measured faster than 4 stages, with the same bits:
+    // about 10% on every 128 x 128 grid and 0.5-1% with 256 x 256 tiles; 2 stages lost 25-30%
     static constexpr int SA = 3;
-    static constexpr int SB = (BM * BN >= 256 * 256) ? 4 : 3;
+    static constexpr int SB = 3;
     static constexpr int DB = SB;                           // steps B is issued ahead
     static constexpr int DA = DB + 1;                       // A half stages issued ahead
     static constexpr int NW = WM * WN;
