@@ -62,10 +62,12 @@ struct SkinnyTraits {
     static constexpr int CHUNKS = ROW_BYTES / 16;          // 16-byte chunks per B row
     static constexpr int A_BYTES = 16 * MT * kSkRows * 2;  // A rows (M padded to 16 MT) x 64 k
     static constexpr int STAGE_BYTES = B_BYTES + A_BYTES;
-    // ring: 96 KB for 128-column strips (5 stages at M <= 16; measured 2-4% faster than 128 KB
-    // with settled clocks, same bits), all of LDS (less the padding sink and the static flag)
-    // for 256-column ones, whose stages are twice as big
-    static constexpr int STAGES = (SW == 128 ? 98304 : 163840 - 2048) / STAGE_BYTES;
+    // ring for 128-column strips: 80 KB (4 stages) for one or two 16-row tiles of M, 96 KB (4
+    // stages) above that; measured with settled clocks against the earlier 128 KB, same bits:
+    // dec_down_M1 22.3 -> 20.4 us, dec_down_M16 22.7 -> 21.0, dec_up_M64 29.3 -> 28.4. All of LDS
+    // (less the padding sink and the static flag) for 256-column strips, whose stages are twice
+    // as big
+    static constexpr int STAGES = (SW == 128 ? (MT <= 2 ? 81920 : 98304) : 163840 - 2048) / STAGE_BYTES;
     static constexpr int DUMMY = STAGES * STAGE_BYTES;     // 1 KB sink for padding loads
     static constexpr int LDS_BYTES = DUMMY + 1024;
     static constexpr int A_INSTR = A_BYTES / 1024;         // 1 KB load instructions for A per stage
