@@ -232,3 +232,60 @@ def test_check_rel_frobenius_bound(oracle_lib):
     # scale every element by (1 + 5e-3): within nothing element-wise, and Frobenius > 4e-3
     scaled = oracle.bf16_rne(ref * (1 + 5e-3))
     assert oracle.check(scaled, ref, sabs).rel_frob > 4e-3
+
+
+# --- the value-only branch (no sum of |a b|) ----------------------------------------------------
+# The bit-exact GPU checks take their expected bits from oracle.gemm(..., with_abs=False), which
+# runs a loop of its own in oracle.c. It is pinned here like the other branch: exact integer brute
+# force with ragged shapes and leading dimensions, closed forms, numpy's float64 product, and bit
+# equality with the pinned with_abs=True branch (both add the K products of an element in
+# ascending k, so the bits must agree).
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 7, 5), (9, 17, 33), (5, 31, 64), (2, 65, 3), (13, 8, 129)])
+def test_value_only_integer_brute_force(oracle_lib, M, N, K):
+    A = matrix("int", M, K, seed=300 + K, ld=K + 3)
+    B = matrix("int", K, N, seed=400 + N, ld=N + 5)
+    a = widen(A[:, :K]).astype(np.int64).tolist()
+    b = widen(B[:, :N]).astype(np.int64).tolist()
+    want = [[float(sum(a[i][k] * b[k][j] for k in range(K))) for j in range(N)] for i in range(M)]
+    ref, sabs = oracle.gemm(A, B, M=M, N=N, K=K, with_abs=False)
+    assert sabs is None
+    assert ref.tolist() == want
+
+
+def test_value_only_closed_forms(oracle_lib):
+    for (M, N, K) in ((3, 5, 7), (2, 9, 11008), (1, 4, 16384)):
+        ref, _ = oracle.gemm(matrix("ones", M, K), matrix("ones", K, N), with_abs=False)
+        assert np.all(ref == K)
+    n = 40
+    A = matrix("normal", 23, n, seed=31)
+    perm = np.random.default_rng(9).permutation(n)
+    ref, _ = oracle.gemm(A, f32_to_bf16_bits(np.eye(n, dtype=np.float32)), with_abs=False)
+    np.testing.assert_array_equal(oracle.bf16_rne(ref), A)
+    ref, _ = oracle.gemm(A, f32_to_bf16_bits(np.eye(n, dtype=np.float32)[:, perm]), with_abs=False)
+    np.testing.assert_array_equal(oracle.bf16_rne(ref), A[:, perm])
+    Bm = matrix("normal", n, 19, seed=32)
+    ref, _ = oracle.gemm(f32_to_bf16_bits(np.eye(n, dtype=np.float32)[perm, :]), Bm, with_abs=False)
+    np.testing.assert_array_equal(oracle.bf16_rne(ref), Bm[perm, :])
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 80, 96), (33, 257, 300), (7, 1000, 1031)])
+def test_value_only_matches_numpy_and_the_pinned_branch(oracle_lib, M, N, K):
+    A = matrix("normal", M, K, seed=41, ld=K + 8)
+    B = matrix("normal", K, N, seed=42, sigma=0.02, ld=N + 8)
+    ref0, _ = oracle.gemm(A, B, M=M, N=N, K=K, with_abs=False)
+    ref1, sabs = oracle.gemm(A, B, M=M, N=N, K=K, with_abs=True)
+    np.testing.assert_array_equal(ref0, ref1)          # same bits as the pinned branch
+    want = widen(A[:, :K]) @ widen(B[:, :N])
+    assert np.all(np.abs(ref0 - want) <= (K + 1) * 2.0 ** -52 * sabs)
+    # row ranges of the value-only branch land on the same rows
+    r2, s2 = oracle.gemm_rows(A, B, 3, 4, N, K, with_abs=False)
+    assert s2 is None
+    np.testing.assert_array_equal(r2, ref0[3:7])
+    # and integer inputs round to the exact bf16 of the exact integer sum
+    Ai = matrix("int", M, K, seed=43)
+    Bi = matrix("int", K, N, seed=44)
+    ri, _ = oracle.gemm(Ai, Bi, with_abs=False)
+    exact = widen(Ai).astype(np.int64) @ widen(Bi).astype(np.int64)
+    np.testing.assert_array_equal(ri, exact.astype(np.float64))
+    np.testing.assert_array_equal(oracle.bf16_rne(ri), f32_to_bf16_bits(exact.astype(np.float32)))
