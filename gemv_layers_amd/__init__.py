@@ -34,7 +34,7 @@ EXPORTS = (
     "gemm_plan_describe",
     "gemm_wave_efficiency", "gemm_last_plan", "gemm_status_string", "gemm_finalize",
     "gemm_peak_mfma_launch", "gemm_peak_copy_launch", "gemm_peak_read_launch",
-    "gemm_peak_clock_launch",
+    "gemm_peak_clock_launch", "gemm_peak_xcc_launch",
     "gemm_peak_empty_launch", "gemm_fill_launch",
     "gemm_mx_packed_sizes", "gemm_mx_pack_weight", "gemm_mx_quantize_act", "gemm_mx_decode",
     "gemm_mx_decode_bf16", "gemm_pack_weight_bf16", "gemm_bf16_packed",
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_peak_read_launch.restype = i32
     L.gemm_peak_clock_launch.argtypes = [i64, i32, p, p]
     L.gemm_peak_clock_launch.restype = i32
+    L.gemm_peak_xcc_launch.argtypes = [i32, p, p]
+    L.gemm_peak_xcc_launch.restype = i32
     L.gemm_peak_empty_launch.argtypes = [p]
     L.gemm_peak_empty_launch.restype = i32
     L.gemm_fill_launch.argtypes = [p, i64, u32, p]
@@ -217,6 +219,10 @@ def gemm_peak_read_launch(src, nbytes, sink, stream=None) -> None:
 
 def gemm_peak_clock_launch(iters, blocks, out, stream=None) -> None:
     _check("gemm_peak_clock_launch", lib().gemm_peak_clock_launch(iters, blocks, out, stream))
+
+
+def gemm_peak_xcc_launch(blocks, out, stream=None) -> None:
+    _check("gemm_peak_xcc_launch", lib().gemm_peak_xcc_launch(blocks, out, stream))
 
 
 def gemm_peak_empty_launch(stream=None) -> None:

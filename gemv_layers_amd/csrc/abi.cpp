@@ -18,27 +18,82 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-// Workspace per device: float32 partial slots for split tiles / K slices, and their counters.
-constexpr int64_t kWsFloats = int64_t(32) << 20;  // 128 MiB
+// Workspace region, one per (device, stream): float32 partial slots for split tiles / K slices,
+// and their arrival counters. On 256 CUs no plan needs more than 4 Mi floats of partials (16 MiB:
+// 256 split pieces of a 128 x 128 tile, or two 16 x 64 x 128 skinny slots per workgroup).
+constexpr int64_t kWsFloats = int64_t(8) << 20;   // 32 MiB
 constexpr int64_t kWsCounters = int64_t(1) << 16;
-// The last 16 MiB of the workspace hold the MXFP8 activations that gemm_mx_decode_bf16 quantises
+// The last 16 MiB of a region hold the MXFP8 activations that gemm_mx_decode_bf16 quantises
 // before its product; MX plans keep their partial slots below them.
 constexpr int64_t kMxActBytes = int64_t(16) << 20;
 constexpr int64_t kMxPartialFloats = kWsFloats - kMxActBytes / 4;
+// Streams with a region of their own, per device. A further stream gets GEMM_ERR_UNSUPPORTED.
+constexpr int kMaxStreams = 64;
+
+// One stream's workspace. Its counters start at zero (cleared when the region is made) and every
+// kernel that uses them returns them to zero, so the region is never cleared again.
+struct Region {
+    hipStream_t stream = nullptr;
+    float* ws = nullptr;
+    uint32_t* counters = nullptr;
+};
 
 struct DeviceState {
     // set (release) by gemm_init once the rest of the state is written; compute calls read it
     // (acquire) without taking the lock
     std::atomic<bool> ready{false};
     glk::DeviceInfo info;
-    float* ws = nullptr;
-    uint32_t* counters = nullptr;
+    std::mutex mu;             // guards the region table
+    Region regions[kMaxStreams];
+    int nregions = 0;
+    hipStream_t clear_stream = nullptr;  // library-private: clears the counters of new regions
 };
 
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 std::atomic<int> g_ready_count{0};
 std::string g_last_plan = "{}";
+
+// The workspace region of `stream` on the device of `ds` (the current device), made on the
+// stream's first call that needs one. Split partials and counters of concurrent calls on
+// different streams then never meet; calls on one stream run in order and share its region.
+// A region is made with hipMalloc in the relaxed capture mode, so that a first call inside a
+// graph capture can still make it: the allocation is not a stream operation, and the counters
+// are cleared on a library-private stream and waited for before the call enqueues anything, so
+// the capture records no memset. A captured graph keeps using the region of the stream it was
+// captured on.
+int region_for(DeviceState& ds, hipStream_t stream, Region** out) {
+    std::lock_guard<std::mutex> lk(ds.mu);
+    for (int i = 0; i < ds.nregions; ++i) {
+        if (ds.regions[i].stream == stream) {
+            *out = &ds.regions[i];
+            return GEMM_OK;
+        }
+    }
+    if (ds.nregions == kMaxStreams) return GEMM_ERR_UNSUPPORTED;
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    if (hipThreadExchangeStreamCaptureMode(&mode) != hipSuccess) return GEMM_ERR_HIP;
+    const size_t cbytes = kWsCounters * sizeof(uint32_t);
+    void* mem = nullptr;
+    int rc = GEMM_OK;
+    if (hipMalloc(&mem, cbytes + kWsFloats * sizeof(float)) != hipSuccess) {
+        mem = nullptr;
+        rc = GEMM_ERR_HIP;
+    }
+    if (rc == GEMM_OK && (hipMemsetAsync(mem, 0, cbytes, ds.clear_stream) != hipSuccess ||
+                          hipStreamSynchronize(ds.clear_stream) != hipSuccess))
+        rc = GEMM_ERR_HIP;
+    if (rc != GEMM_OK && mem) hipFree(mem);
+    hipThreadExchangeStreamCaptureMode(&mode);
+    if (rc != GEMM_OK) return rc;
+    Region& r = ds.regions[ds.nregions];
+    r.stream = stream;
+    r.counters = static_cast<uint32_t*>(mem);
+    r.ws = reinterpret_cast<float*>(static_cast<char*>(mem) + cbytes);
+    ++ds.nregions;
+    *out = &r;
+    return GEMM_OK;
+}
 
 int copy_out(const std::string& s, char* buf, int len) {
     if (!buf || len <= 0) return GEMM_ERR_INVALID_ARG;
@@ -84,6 +139,11 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
     const glk::Plan p = glk::make_plan(M, N, K, ds.info, fast, force, glu);
     // (no buffer that fits in device memory gets here; the launch takes a 32-bit grid)
     if (p.grid > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
+    Region* rg = nullptr;
+    if (p.kernel == glk::kKernTile || p.kernel == glk::kKernSkinny) {
+        st = region_for(ds, stream, &rg);
+        if (st != GEMM_OK) return st;
+    }
     const uint16_t* a16 = static_cast<const uint16_t*>(A);
     const uint16_t* b16 = static_cast<const uint16_t*>(B);
     uint16_t* c16 = static_cast<uint16_t*>(C);
@@ -115,8 +175,8 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
             t.sched = p.sched;
             t.splits = p.splits;
             t.kt_per_split = p.kt_per_split;
-            t.ws = ds.ws;
-            t.counters = ds.counters;
+            t.ws = rg->ws;
+            t.counters = rg->counters;
             e = glk::launch_tile_gemm(p.tile_cfg, t, (int)p.grid, glu, stream);
             break;
         }
@@ -136,8 +196,8 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
             s.grid = (int)p.grid;
             s.split = glk::make_unit_split(p.strips * p.ks, (int)p.grid);
             s.nxcd = p.nxcd;
-            s.ws = ds.ws;
-            s.counters = ds.counters;
+            s.ws = rg->ws;
+            s.counters = rg->counters;
             e = glk::launch_skinny_gemm(p.mtiles, p.strip, glu, s, stream);
             break;
         }
@@ -231,6 +291,9 @@ int mx_decode(int64_t M, int64_t N, int64_t K, const void* Aq, int64_t ldaq, con
     if (p.kernel == glk::kKernZero) {
         e = glk::launch_zero_c(static_cast<uint16_t*>(C), M, N, ldc, stream);
     } else {
+        Region* rg = nullptr;
+        st = region_for(*ds, stream, &rg);
+        if (st != GEMM_OK) return st;
         glk::MxArgs a;
         a.Aq = static_cast<const uint8_t*>(Aq);
         a.As = static_cast<const uint8_t*>(As);
@@ -248,8 +311,8 @@ int mx_decode(int64_t M, int64_t N, int64_t K, const void* Aq, int64_t ldaq, con
         a.kq = (a.ks + 3) / 4;
         a.pieces = p.splits;
         a.nxcd = p.nxcd;
-        a.ws = ds->ws;
-        a.counters = ds->counters;
+        a.ws = rg->ws;
+        a.counters = rg->counters;
         a.A16 = static_cast<const uint16_t*>(A16);
         a.lda16 = (int)lda16;
         a.kpb = 0;
@@ -290,6 +353,9 @@ int packed_decode(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, c
     if (p.kernel == glk::kKernZero) {
         e = glk::launch_zero_c(static_cast<uint16_t*>(C), M, N, ldc, stream);
     } else {
+        Region* rg = nullptr;
+        st = region_for(*ds, stream, &rg);
+        if (st != GEMM_OK) return st;
         glk::PkArgs a;
         a.A = static_cast<const uint16_t*>(A);
         a.Bp = static_cast<const uint16_t*>(Bp);
@@ -303,8 +369,8 @@ int packed_decode(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, c
         a.ks = (int)(K / 32);
         a.pieces = p.splits;
         a.nxcd = p.nxcd;
-        a.ws = ds->ws;
-        a.counters = ds->counters;
+        a.ws = rg->ws;
+        a.counters = rg->counters;
         e = glk::launch_pk_decode(p.mtiles, p.strip / 16, a, (int)p.grid, stream);
     }
     if (e != hipSuccess) return GEMM_ERR_HIP;
@@ -332,30 +398,30 @@ int gemm_init(int device) {
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK) {
         ds.info.cus = prop.multiProcessorCount;
-        ds.info.nxcd = 8;  // MI355X: 8 XCDs, workgroups dealt round robin
-        if (ds.info.cus % ds.info.nxcd != 0) ds.info.nxcd = 1;
+        // the XCDs (accelerator complex dies) the dispatcher deals workgroups to, round robin;
+        // the tile orders keep each XCD's share contiguous (a bijection for any count)
+        int xcc = 1;
+        if (hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, device) != hipSuccess || xcc < 1)
+            xcc = 1;
+        ds.info.nxcd = (ds.info.cus % xcc == 0) ? xcc : 1;
         ds.info.ws_floats = kWsFloats;
         ds.info.ws_counters = kWsCounters;
         if (const char* f = getenv("GEMM_BF16_FORCE_TILE")) ds.info.force_tile_cfg = atoi(f);
-        if (hipMalloc(&ds.ws, kWsFloats * sizeof(float)) != hipSuccess) rc = GEMM_ERR_HIP;
+        if (hipStreamCreateWithFlags(&ds.clear_stream, hipStreamNonBlocking) != hipSuccess) {
+            ds.clear_stream = nullptr;
+            rc = GEMM_ERR_HIP;
+        }
     }
-    if (rc == GEMM_OK && hipMalloc(&ds.counters, kWsCounters * sizeof(uint32_t)) != hipSuccess)
-        rc = GEMM_ERR_HIP;
-    if (rc == GEMM_OK && hipMemset(ds.counters, 0, kWsCounters * sizeof(uint32_t)) != hipSuccess)
-        rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_skinny_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_tile_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_mx_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_pk_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
-    if (rc == GEMM_OK && hipDeviceSynchronize() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK) {
         ds.ready.store(true, std::memory_order_release);
         ++g_ready_count;
-    } else {
-        if (ds.ws) hipFree(ds.ws);
-        if (ds.counters) hipFree(ds.counters);
-        ds.ws = nullptr;
-        ds.counters = nullptr;
+    } else if (ds.clear_stream) {
+        hipStreamDestroy(ds.clear_stream);
+        ds.clear_stream = nullptr;
     }
     hipSetDevice(prev);
     return rc;
@@ -446,10 +512,14 @@ int gemm_finalize(void) {
         int prev = -1;
         hipGetDevice(&prev);
         hipSetDevice(d);
-        if (ds.ws && hipFree(ds.ws) != hipSuccess) rc = GEMM_ERR_HIP;
-        if (ds.counters && hipFree(ds.counters) != hipSuccess) rc = GEMM_ERR_HIP;
-        ds.ws = nullptr;
-        ds.counters = nullptr;
+        std::lock_guard<std::mutex> rl(ds.mu);
+        for (int i = 0; i < ds.nregions; ++i) {
+            if (hipFree(ds.regions[i].counters) != hipSuccess) rc = GEMM_ERR_HIP;
+            ds.regions[i] = Region();
+        }
+        ds.nregions = 0;
+        if (ds.clear_stream && hipStreamDestroy(ds.clear_stream) != hipSuccess) rc = GEMM_ERR_HIP;
+        ds.clear_stream = nullptr;
         ds.ready.store(false, std::memory_order_release);
         hipSetDevice(prev);
     }
@@ -515,7 +585,10 @@ int gemm_mx_decode_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
     // the quantised activations go to the workspace tail (both launches on the same stream)
     const int64_t ldaq = (K + 15) / 16 * 16, ldas = K / 32;
     if (M * ldaq + M * ldas + 16 > kMxActBytes) return GEMM_ERR_UNSUPPORTED;
-    uint8_t* base = reinterpret_cast<uint8_t*>(ds->ws + kMxPartialFloats);
+    Region* rg = nullptr;
+    st = region_for(*ds, hs, &rg);
+    if (st != GEMM_OK) return st;
+    uint8_t* base = reinterpret_cast<uint8_t*>(rg->ws + kMxPartialFloats);
     uint8_t* aq = base;
     uint8_t* as = base + (M * ldaq + 15) / 16 * 16;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -575,6 +648,13 @@ int gemm_peak_read_launch(const void* src, int64_t bytes, uint32_t* sink, gemm_s
 int gemm_peak_clock_launch(int64_t iters, int blocks, uint64_t* out, gemm_stream_t stream) {
     if (iters < 0 || blocks <= 0 || !out) return GEMM_ERR_INVALID_ARG;
     return glk::launch_peak_clock(iters, blocks, out, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
+int gemm_peak_xcc_launch(int blocks, uint32_t* out, gemm_stream_t stream) {
+    if (blocks <= 0 || !out) return GEMM_ERR_INVALID_ARG;
+    return glk::launch_peak_xcc(blocks, out, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
                ? GEMM_OK
                : GEMM_ERR_HIP;
 }

@@ -142,5 +142,6 @@ hipError_t launch_peak_copy(const void* src, void* dst, int64_t bytes, hipStream
 hipError_t launch_peak_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_peak_empty(hipStream_t s);
 hipError_t launch_peak_clock(int64_t iters, int blocks, uint64_t* out, hipStream_t s);
+hipError_t launch_peak_xcc(int blocks, uint32_t* out, hipStream_t s);
 
 }  // namespace glk

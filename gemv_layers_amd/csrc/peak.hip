@@ -110,6 +110,20 @@ __global__ void __launch_bounds__(64) peak_clock_kernel(int64_t iters, uint64_t*
     }
 }
 
+// Placement probe: each workgroup records the XCD (accelerator complex die) it runs on, from the
+// XCC_ID hardware register (its low 4 bits). The tile and strip orders assume that the dispatcher
+// deals consecutive workgroups to the XCDs round robin; this probe lets a test check it.
+__global__ void __launch_bounds__(64) peak_xcc_kernel(uint32_t* out) {
+    uint32_t x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    if (threadIdx.x == 0) out[blockIdx.x] = x & 15u;
+}
+
+hipError_t launch_peak_xcc(int blocks, uint32_t* out, hipStream_t s) {
+    peak_xcc_kernel<<<blocks, 64, 0, s>>>(out);
+    return hipGetLastError();
+}
+
 hipError_t launch_peak_mfma(int64_t iters, int blocks, float* sink, uint64_t* cycles, hipStream_t s) {
     peak_mfma_kernel<<<blocks, 256, 0, s>>>(iters, sink, cycles);
     return hipGetLastError();

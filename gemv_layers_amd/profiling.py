@@ -7,6 +7,8 @@
 
     python -m gemv_layers_amd.profiling window <run_kernel_trace.csv> --kernel REGEX --skip N
         --count K [--grid THREADS]
+    python -m gemv_layers_amd.profiling counters <counter_collection.csv> [...] --kernel REGEX
+        [--grid THREADS] [--cus N] [--command CMD]
 
 `stats` prints the per-kernel table of a `--kernel-trace --stats --output-format csv` run (the
 kernels matching REGEX only, when given).
@@ -14,6 +16,11 @@ kernels matching REGEX only, when given).
 prints the mean, minimum and maximum duration of the next K, and their span (first start to
 last end) divided by K: e.g. the timed region of a benchmark that runs N warm-up launches
 first.
+`counters` averages every counter of one or more `--pmc` passes over the dispatches of the
+matching kernel and derives the busy fractions: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over
+(GRBM_GUI_ACTIVE x CUs x 4 SIMDs), wave wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, TA busy =
+TA_TA_BUSY over (GRBM_GUI_ACTIVE x CUs), TA address FIFO full = SQ_VMEM_TA_ADDR_FIFO_FULL over
+(GRBM_GUI_ACTIVE x CUs), and LDS bank conflicts per LDS instruction.
 `traffic` turns two counter passes (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, both over a
 command that also runs the library's copy kernel on `--copy-bytes` bytes, e.g.
 `bench.py --copy-calibration`) into HBM bytes per launch of the kernel matching REGEX: each
@@ -156,6 +163,57 @@ def cmd_traffic(a) -> None:
         print(f"traffic_over_algorithmic: {(fetch_b + write_b) / a.algorithmic_bytes:.3f}")
 
 
+def counter_means(paths, kernel_regex: str, grid: int = 0) -> tuple[dict, dict]:
+    """Mean per dispatch of every counter of the matching kernel over the given passes, and the
+    number of dispatches each mean is over."""
+    rx = re.compile(kernel_regex)
+    vals: dict[str, list[float]] = {}
+    for path in paths:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if rx.search(r["Kernel_Name"]) and (not grid or int(r["Grid_Size"]) == grid):
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: _mean(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+def derived_fractions(m: dict, cus: int) -> dict:
+    out = {}
+    gui = m.get("GRBM_GUI_ACTIVE")
+    if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+        out["mfma_busy_frac"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * cus * 4)
+    if "SQ_WAIT_INST_ANY" in m and m.get("SQ_WAVE_CYCLES"):
+        out["wave_wait_inst_frac"] = m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"]
+    if "SQ_WAIT_ANY" in m and m.get("SQ_WAVE_CYCLES"):
+        out["wave_wait_any_frac"] = m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"]
+    if gui and "TA_TA_BUSY" in m:
+        out["ta_busy_frac"] = m["TA_TA_BUSY"] / (gui * cus)
+    if gui and "TA_ADDR_STALLED_BY_TC_CYCLES" in m:
+        out["ta_addr_stalled_by_tc_frac"] = m["TA_ADDR_STALLED_BY_TC_CYCLES"] / (gui * cus)
+    if gui and "SQ_VMEM_TA_ADDR_FIFO_FULL" in m:
+        out["ta_addr_fifo_full_frac"] = m["SQ_VMEM_TA_ADDR_FIFO_FULL"] / (gui * cus)
+    if m.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in m:
+        out["lds_bank_conflict_cycles_per_lds_inst"] = m["SQ_LDS_BANK_CONFLICT"] / m["SQ_INSTS_LDS"]
+    if m.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in m:
+        out["lds_bank_conflict_per_active_lds_cycle"] = m["SQ_LDS_BANK_CONFLICT"] / m["SQ_ACTIVE_INST_LDS"]
+    if m.get("TCC_HIT") is not None and m.get("TCC_MISS") is not None and (m["TCC_HIT"] + m["TCC_MISS"]) > 0:
+        out["l2_hit_frac"] = m["TCC_HIT"] / (m["TCC_HIT"] + m["TCC_MISS"])
+    return out
+
+
+def cmd_counters(a) -> None:
+    means, counts = counter_means(a.csv, a.kernel, a.grid)
+    if not means:
+        raise SystemExit("no matching dispatches")
+    print(f"# mean per dispatch of the kernel matching /{a.kernel}/" + (f", grid {a.grid} threads" if a.grid else ""))
+    if a.command:
+        for ln in a.command.split(" ;; "):
+            print(f"# command: {ln}")
+    for k in sorted(means):
+        print(f"{k}: {means[k]:.1f}   # {counts[k]} dispatches")
+    for k, v in derived_fractions(means, a.cus).items():
+        print(f"{k}: {v:.4f}")
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(prog="python -m gemv_layers_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -180,8 +238,14 @@ def main(argv=None) -> None:
     w.add_argument("--skip", type=int, default=0)
     w.add_argument("--count", type=int, required=True)
     w.add_argument("--grid", type=int, default=0, help="only dispatches with this many threads")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--grid", type=int, default=0, help="only dispatches with this many threads")
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--command", default="")
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic, "window": cmd_window}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "window": cmd_window, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":

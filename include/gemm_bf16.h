@@ -41,12 +41,13 @@ typedef enum {
 } gemm_status_t;
 
 /*
- * gemm_init: prepare the library for HIP device `device` (queries the device's compute-unit
- * count and LDS size for the planner, and allocates the library-owned workspace used by split
- * tiles: float32 partial slots plus counters, zeroed once here and returned to zero by the
- * kernels that use them, so no call ever needs a memset). Call it outside graph capture, before
- * the first compute call on that device. Calling it again for an initialised device is a no-op.
- * Returns GEMM_ERR_HIP when the device cannot be used.
+ * gemm_init: prepare the library for HIP device `device`: queries the device's compute-unit
+ * count and XCD count for the planner ("Kernel development on sm_120", section 1: query every
+ * hardware number rather than hard-coding it) and sets the kernels' LDS limits. Allocates no
+ * workspace: each stream gets its own region on its first call that needs one (see gemm_bf16).
+ * Call it outside graph capture, before the first compute call on that device. Calling it again
+ * for an initialised device is a no-op. Returns GEMM_ERR_INVALID_ARG for a negative device
+ * number and GEMM_ERR_HIP when the device cannot be used.
  */
 int gemm_init(int device);
 
@@ -62,8 +63,17 @@ int gemm_init(int device);
  * Errors: GEMM_ERR_INVALID_ARG for negative sizes, lda < K, ldb < N, ldc < N, or a null
  * pointer with a non-empty extent; GEMM_ERR_NOT_INITIALIZED before gemm_init; GEMM_ERR_HIP if a
  * launch fails. The call is deterministic: the same inputs give the same bits on every run.
- * Two calls that run concurrently on different streams of one device share the workspace and
- * must be serialised by the caller.
+ * Workspace: split layouts sum float32 partials in K order through slots and arrival counters
+ * that the kernel itself returns to zero, so a call is one launch with no memset (spark-kernels
+ * post, "stream-k proper": nothing cleared between launches; "the decode kernel": the last slice
+ * resets the workspace so a call stays one launch). The slots and counters live in a region per
+ * (device, stream), made on the stream's first call that needs one (hipMalloc, plus a clear on a
+ * library-private stream that is waited for, so that even a first call inside a graph capture
+ * records only the product's kernel). Calls on different streams therefore never share partials
+ * and may run concurrently; calls on one stream run in order. A captured graph keeps using the
+ * region of the stream it was captured on, so it must not be replayed concurrently with calls on
+ * that stream. At most 64 streams per device get a region; a call on a further stream that needs
+ * one returns GEMM_ERR_UNSUPPORTED.
  */
 int gemm_bf16(int64_t M, int64_t N, int64_t K,
               const void *A, int64_t lda,
@@ -110,8 +120,8 @@ int gemm_bf16_tiled(int64_t M, int64_t N, int64_t K,
  * M == 0 or N == 0: nothing is launched. K == 0: C is set to zero (silu(0) * 0).
  * Errors: GEMM_ERR_INVALID_ARG for negative sizes, lda < K, ldb < 2N, ldc < N, or a null pointer
  * with a non-empty extent; GEMM_ERR_NOT_INITIALIZED before gemm_init; GEMM_ERR_HIP if a launch
- * fails. Deterministic, enqueued on `stream` without synchronising (capturable), and sharing the
- * device workspace with the other compute calls (concurrent calls must be serialised).
+ * fails. Deterministic, enqueued on `stream` without synchronising (capturable), and using the
+ * stream's workspace region like gemm_bf16.
  */
 int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K,
                      const void *A, int64_t lda,
@@ -169,7 +179,7 @@ int gemm_mx_quantize_act(int64_t M, int64_t K, const void *A, int64_t lda, void 
  * gemm_mx_quantize_act) and MXFP4 weights (packed by gemm_mx_pack_weight). C is M x N bf16
  * (ldc >= N, ldc % 4 == 0, 8-byte aligned). Requires M <= 64, N % 16 == 0, K % 128 == 0
  * (GEMM_ERR_UNSUPPORTED otherwise). M == 0 or N == 0: nothing; K == 0: C = 0. One launch;
- * deterministic; shares the device workspace like the other compute calls.
+ * deterministic; uses the stream's workspace region like gemm_bf16.
  */
 int gemm_mx_decode(int64_t M, int64_t N, int64_t K, const void *Aq, int64_t ldaq, const void *As,
                    int64_t ldas, const void *Wp, const void *Sp, void *C, int64_t ldc,
@@ -177,9 +187,10 @@ int gemm_mx_decode(int64_t M, int64_t N, int64_t K, const void *Aq, int64_t ldaq
 
 /*
  * gemm_mx_decode_bf16: gemm_mx_quantize_act into the library's workspace, then gemm_mx_decode
- * (two launches on `stream`): the decode product from bf16 activations A (M x K, lda >= K,
- * lda % 8 == 0, 16-byte aligned) and packed MXFP4 weights. Same requirements and results as the
- * two calls.
+ * (two launches on `stream`; for M <= 2 one launch that converts inside the product): the decode
+ * product from bf16 activations A (M x K, lda >= K, lda % 8 == 0, 16-byte aligned) and packed MXFP4
+ * weights. The quantised activations go to the tail of the stream's workspace region. Same
+ * requirements and results as the two calls.
  */
 int gemm_mx_decode_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *Wp,
                         const void *Sp, void *C, int64_t ldc, gemm_stream_t stream);
@@ -207,8 +218,8 @@ int gemm_pack_weight_bf16(int64_t K, int64_t N, const void *B, int64_t ldb, void
  * gemm_bf16_packed: C = A * B for 1 <= M <= 64 with B packed by gemm_pack_weight_bf16. A is M x K
  * bf16 (lda >= K, lda % 8 == 0, 16-byte aligned), C is M x N bf16 (ldc >= N, ldc % 4 == 0, 8-byte
  * aligned). Requires M <= 64, N % 16 == 0, K % 32 == 0 (GEMM_ERR_UNSUPPORTED otherwise).
- * M == 0 or N == 0: nothing; K == 0: C = 0. One launch; deterministic; shares the device
- * workspace like the other compute calls.
+ * M == 0 or N == 0: nothing; K == 0: C = 0. One launch; deterministic; uses the stream's
+ * workspace region like gemm_bf16.
  */
 int gemm_bf16_packed(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *Bp,
                      void *C, int64_t ldc, gemm_stream_t stream);
@@ -238,14 +249,36 @@ int gemm_plan_describe(int64_t M, int64_t N, int64_t K, int cus, int flags, char
  */
 int gemm_wave_efficiency(int64_t ctas, int64_t slots, double *efficiency, int64_t *waves);
 
-/* gemm_last_plan: the JSON plan of the last successful compute call (any device) into buf. */
+/*
+ * gemm_last_plan: the JSON plan (the same fields as gemm_plan_describe) of the last successful
+ * compute call in this process, any device or stream, copied into buf (len bytes, always
+ * NUL-terminated when len > 0). The plan is chosen per call from the shape and the device, so
+ * this is how a benchmark or test reads which kernel, tile and split a call took (spark-kernels
+ * post, "1024 cubed and the decode shapes": the launch picks the tile per call). Host-only; touches
+ * no HIP state. GEMM_ERR_INVALID_ARG for a null buf, len <= 0, or a plan longer than len - 1
+ * (buf then holds the truncated text).
+ */
 int gemm_last_plan(char *buf, int len);
 
-/* gemm_status_string: a static, human-readable name for a status code. */
+/*
+ * gemm_status_string: a static, human-readable name for a status code ("GEMM_ERR_UNKNOWN" for a
+ * value outside gemm_status_t). Every entry point returns a status and never throws, so that a
+ * benchmark or test reports a refused or failed call by name instead of timing it as if it had
+ * run ("Kernel development on sm_120", section 6, "Benchmarking": the benchmark is audited as
+ * carefully as the kernel, since several of that repository's bugs were benchmark bugs). Never
+ * null; the caller must not free it.
+ */
 const char *gemm_status_string(int status);
 
-/* gemm_finalize: release the workspaces of every initialised device (call outside capture,
- * after the caller's streams have drained). */
+/*
+ * gemm_finalize: frees every stream's workspace region and the private stream of every
+ * initialised device, and returns the devices to the uninitialised state (gemm_init may be called
+ * again). The workspaces are the library's only allocations, the ones gemm_init's contract says
+ * the library owns (spark-kernels post, "stream-k proper" and "the decode kernel": partial slots
+ * and counters that persist between launches instead of being cleared per call). Call it outside
+ * graph capture, after every stream that used the library has drained and after any graph that
+ * holds its kernels has been destroyed. GEMM_ERR_HIP if a free fails (the rest are still freed).
+ */
 int gemm_finalize(void);
 
 /* ------------------------------------------------------------------------------------------
@@ -287,6 +320,15 @@ int gemm_peak_empty_launch(gemm_stream_t stream);
  * (the clock changes over milliseconds, the probe lasts microseconds).
  */
 int gemm_peak_clock_launch(int64_t iters, int blocks, uint64_t *out, gemm_stream_t stream);
+
+/*
+ * gemm_peak_xcc_launch: `blocks` workgroups of one wave each write, to out[b] (device, >= blocks
+ * uint32), the index of the XCD (accelerator complex die) that workgroup b ran on. The planner's
+ * tile and strip orders assume consecutive workgroups are dealt to the XCDs round robin, each
+ * XCD with its own L2; this measures the assumption instead of quoting it ("Kernel development on
+ * sm_120", section 1: query or measure every hardware number).
+ */
+int gemm_peak_xcc_launch(int blocks, uint32_t *out, gemm_stream_t stream);
 
 /* gemm_fill_launch: writes the 32-bit `value` over dst[0 .. bytes) (bytes % 4 == 0); used to
  * evict the device's caches between timed calls and to poison outputs before checks. */

@@ -284,15 +284,23 @@ def test_workload_all_ones_every_element(name):
     assert bad == 0, f"{name}: {bad} elements differ from K = {w.K}"
 
 
-@pytest.mark.parametrize("name", ["sq4096", "mlp_up", "mlp_down", "dec_up_M64", "dec_down_M16"])
-def test_workload_integer_exact_sampled(name):
-    w = WORKLOADS[name]
-    A = matrix("int", w.M, w.K, seed=w.seed_a)
-    B = matrix("int", w.K, w.N, seed=w.seed_b)
-    C = run("auto", A, B, w.M, w.N, w.K)
-    rows = _sample_rows(w.M, 32)
-    ref, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, M=len(rows), N=w.N, K=w.K,
-                         with_abs=False)
+# Integer-valued inputs in {-4 .. 4}: every partial sum is an integer below 16 K <= 2^18, exact in
+# float32 in any order, so the result must equal the oracle's rounding of the exact sum bit for
+# bit. Every workload shape, plus ragged shapes at the same scale (a partial last tile in M, N and
+# K, and a decode shape whose N and K are not multiples of the strip or the stage).
+INT_SHAPES = [(n, WORKLOADS[n].M, WORKLOADS[n].N, WORKLOADS[n].K) for n in FULL] + \
+             [("ragged_prefill", 4000, 11000, 4104), ("ragged_square", 8200, 8200, 8200),
+              ("ragged_decode", 37, 11000, 4100)]
+
+
+@pytest.mark.parametrize("name,M,N,K", INT_SHAPES)
+def test_workload_integer_exact_sampled(name, M, N, K):
+    seed = WORKLOADS[name].seed_a if name in WORKLOADS else 0x5EED1000 + M
+    A = matrix("int", M, K, seed=seed)
+    B = matrix("int", K, N, seed=seed + 1)
+    C = run("auto", A, B, M, N, K)
+    rows = _sample_rows(M, 32 if M * N <= (1 << 26) else 16)
+    ref, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, M=len(rows), N=N, K=K, with_abs=False)
     want = oracle.bf16_rne(ref)
     bad = np.argwhere(C[rows] != want)
     assert bad.size == 0, f"{name}: {len(bad)} mismatches, first {bad[0].tolist()}"
@@ -429,6 +437,29 @@ def test_graph_replay_matches_eager(entry, M, N, K):
 
 # ---- measurement kernels ---------------------------------------------------------------------
 
+def _check_mfma_sink(sink, iters):
+    """The peak loop's accumulators in closed form. Each wave runs 8 identical chains of
+    v_mfma_f32_32x32x16_bf16 on fixed operands: lane l holds row (A) or column (B) l % 32 and
+    k = 8 (l // 32) + e in its element e, with a = 1 + ((l + e) & 7) / 128 and
+    b = 1/2 - ((3 l + e) & 7) / 128. After `iters` steps every chain holds iters * (A B), and
+    lanes l and l + 32 together hold all 32 rows of column l % 32, so the two lanes' sinks add up
+    to 8 * iters * (column sum of A B)."""
+    A = np.zeros((32, 16))
+    B = np.zeros((16, 32))
+    for lane in range(64):
+        for e in range(8):
+            k = 8 * (lane // 32) + e
+            A[lane % 32, k] = 1.0 + ((lane + e) & 7) / 128.0
+            B[k, lane % 32] = 0.5 - ((3 * lane + e) & 7) / 128.0
+    colsum = (A @ B).sum(axis=0)  # exact: multiples of 2^-14 well inside float64
+    want = 8.0 * iters * colsum
+    for wave in range(4):
+        w = sink[:, 64 * wave:64 * wave + 64]
+        got = w[:, :32] + w[:, 32:]
+        assert np.all(np.abs(got - want[None, :]) <= 1e-4 * want[None, :]), \
+            f"wave {wave}: sink {got[0, :4]} against closed form {want[:4]}"
+
+
 def test_measurement_kernels_run_and_copy_is_exact():
     n = 64 << 20
     src = torch.randint(-2**31, 2**31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
@@ -448,8 +479,64 @@ def test_measurement_kernels_run_and_copy_is_exact():
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
     assert torch.all(cyc > 0)
-    assert torch.isfinite(fs).all()
+    _check_mfma_sink(fs.cpu().double().numpy().reshape(blocks, 256), 1000)
     c = clk.view(-1, 2).double().cpu()
     assert torch.all(c > 0)
     ghz = c[:, 0] / c[:, 1] * 0.1  # s_memrealtime ticks at 100 MHz
     assert 0.3 < float(ghz.median()) < 3.0
+
+
+# ---- concurrent streams and XCD placement ------------------------------------------------------
+
+def test_split_layouts_on_two_streams_at_once():
+    # Each stream gets its own workspace region, so split products enqueued on two streams with
+    # no synchronisation between them cannot meet in the partial slots or the arrival counters.
+    # Integer inputs: every result must equal the oracle's rounding of the exact sum bit for bit.
+    cases = [("auto", 16, 4096, 11008),                     # skinny, K split 8 ways
+             ("skinny", 3, 128 * 141 + 8, 64 * 37 + 8),     # Stream-K ranges across strips
+             ("tiled", 1000, 1000, 1000)]                   # 128 x 128 tiles, K split
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for entry, M, N, K in cases:
+        ins, wants, outs = [], [], []
+        for si in range(2):
+            A = matrix("int", M, K, seed=12000 + 10 * si + M)
+            B = matrix("int", K, N, seed=13000 + 10 * si + N)
+            ref, _ = oracle.gemm(A, B, with_abs=False)
+            wants.append(oracle.bf16_rne(ref))
+            ins.append((dev(A), dev(B)))
+            outs.append([torch.empty(M * N, dtype=torch.bfloat16, device="cuda") for _ in range(3)])
+        assert g.gemm_plan_describe(M, N, K, 256, entry == "skinny")["splits"] > 1
+        torch.cuda.synchronize()
+        for rep in range(12):
+            for si in range(2):
+                dA, dB = ins[si]
+                C = outs[si][rep % 3]
+                with torch.cuda.stream(streams[si]):
+                    h = g.current_stream_handle()
+                    g.gemm_fill_launch(ctypes.c_void_p(C.data_ptr()), C.numel() * 2, POISON, h)
+                    ENTRIES[entry](M, N, K, ctypes.c_void_p(dA.data_ptr()), K, ctypes.c_void_p(dB.data_ptr()),
+                                   N, ctypes.c_void_p(C.data_ptr()), N, h)
+        torch.cuda.synchronize()
+        for si in range(2):
+            for C in outs[si]:
+                got = host(C).reshape(M, N)
+                bad = np.argwhere(got != wants[si])
+                assert bad.size == 0, f"{entry} {M}x{N}x{K} stream {si}: {len(bad)} mismatches"
+
+
+def test_workgroups_are_dealt_to_xcds_round_robin():
+    # the tile and strip orders keep each XCD's share contiguous on the assumption that the
+    # dispatcher deals consecutive workgroups to the XCDs in turn; measure it, and check that
+    # the planner took the device's XCD count
+    blocks = 4096
+    out = torch.full((blocks,), 0xFFFF, dtype=torch.int32, device="cuda")
+    g.gemm_peak_xcc_launch(blocks, ctypes.c_void_p(out.data_ptr()), g.current_stream_handle())
+    torch.cuda.synchronize()
+    x = out.cpu().numpy()
+    A = matrix("int", 256, 256, seed=1)
+    B = matrix("int", 256, 256, seed=2)
+    run("tiled", A, B, 256, 256, 256)
+    nxcd = g.gemm_last_plan()["nxcd"]
+    assert nxcd == len(set(x.tolist())), f"planner nxcd {nxcd}, probe saw XCDs {sorted(set(x.tolist()))}"
+    assert len(set(x[:nxcd].tolist())) == nxcd
+    assert np.array_equal(x, np.tile(x[:nxcd], blocks // nxcd)), "workgroups not dealt round robin"

@@ -94,3 +94,24 @@ def test_stats_filters_by_kernel(tmp_path):
     text = _run(["stats", str(p), "--kernel", "glk::"])
     assert "glk::a_kernel" in text and "other" not in text
     assert "1.000" in text  # average in microseconds
+
+
+PMC_HEADER = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def test_counters_average_per_dispatch_and_derive_fractions(tmp_path):
+    p1, p2 = tmp_path / "a.csv", tmp_path / "b.csv"
+    k = "tile_gemm_kernel<256, 256, 2, 4, false>"
+    _write(p1, PMC_HEADER, [
+        [1, 131072, k, "GRBM_GUI_ACTIVE", 1000.0], [1, 131072, k, "SQ_VALU_MFMA_BUSY_CYCLES", 512000.0],
+        [2, 131072, k, "GRBM_GUI_ACTIVE", 3000.0], [2, 131072, k, "SQ_VALU_MFMA_BUSY_CYCLES", 1536000.0],
+        [3, 524288, k, "GRBM_GUI_ACTIVE", 9.0e9], [4, 131072, "other", "GRBM_GUI_ACTIVE", 1.0],
+        [1, 131072, k, "SQ_WAVE_CYCLES", 400.0], [1, 131072, k, "SQ_WAIT_INST_ANY", 100.0],
+        [2, 131072, k, "SQ_WAVE_CYCLES", 400.0], [2, 131072, k, "SQ_WAIT_INST_ANY", 300.0]])
+    _write(p2, PMC_HEADER, [[5, 131072, k, "TA_TA_BUSY", 256000.0], [5, 131072, k, "GRBM_GUI_ACTIVE", 2000.0]])
+    kv = _kv(_run(["counters", str(p1), str(p2), "--kernel", "tile_gemm", "--grid", "131072", "--cus", "256"]))
+    assert float(kv["GRBM_GUI_ACTIVE"].split("#")[0]) == pytest.approx(2000.0)
+    # 1024000 / (2000 * 256 * 4) = 0.5
+    assert float(kv["mfma_busy_frac"]) == pytest.approx(0.5)
+    assert float(kv["wave_wait_inst_frac"]) == pytest.approx(0.5)
+    assert float(kv["ta_busy_frac"]) == pytest.approx(0.5)
