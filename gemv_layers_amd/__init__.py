@@ -30,7 +30,7 @@ GEMM_PLAN_PACKED = 8
 
 # every symbol include/gemm_bf16.h declares
 EXPORTS = (
-    "gemm_init", "gemm_bf16", "gemm_bf16_skinny", "gemm_bf16_tiled", "gemm_bf16_swiglu",
+    "gemm_init", "gemm_bf16", "gemm_bf16_noalloc", "gemm_bf16_skinny", "gemm_bf16_tiled", "gemm_bf16_swiglu",
     "gemm_plan_describe",
     "gemm_wave_efficiency", "gemm_last_plan", "gemm_status_string", "gemm_finalize",
     "gemm_peak_mfma_launch", "gemm_peak_copy_launch", "gemm_peak_read_launch",
@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     i64, i32, p, u32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint32
     gemm_sig = [i64, i64, i64, p, i64, p, i64, p, i64, p]
-    for name in ("gemm_bf16", "gemm_bf16_skinny", "gemm_bf16_tiled", "gemm_bf16_swiglu"):
+    for name in ("gemm_bf16", "gemm_bf16_noalloc", "gemm_bf16_skinny", "gemm_bf16_tiled", "gemm_bf16_swiglu"):
         getattr(L, name).argtypes = gemm_sig
         getattr(L, name).restype = i32
     L.gemm_init.argtypes = [i32]
@@ -137,6 +137,11 @@ def _call(name, M, N, K, A, lda, B, ldb, C, ldc, stream):
 def gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
     """C = A * B on raw device pointers (ints); see include/gemm_bf16.h."""
     _call("gemm_bf16", M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_bf16_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
+    """gemm_bf16 with the library's fixed scratch array as workspace (never allocates)."""
+    _call("gemm_bf16_noalloc", M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def gemm_bf16_skinny(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:

@@ -38,6 +38,13 @@ struct Region {
     uint32_t* counters = nullptr;
 };
 
+// Workspace of gemm_bf16_noalloc, for callers that cannot allocate: a file-scope device array
+// (each GPU the library runs on holds its own copy until the process ends), arrival counters
+// first, then float32 partial slots. 4 Mi floats hold the largest split plan on 256 CUs.
+constexpr int64_t kScratchCounters = int64_t(1) << 14;   // 64 KiB
+constexpr int64_t kScratchFloats = int64_t(4) << 20;     // 16 MiB
+static __device__ __align__(256) uint32_t scratch[kScratchCounters + kScratchFloats];
+
 struct DeviceState {
     // set (release) by gemm_init once the rest of the state is written; compute calls read it
     // (acquire) without taking the lock
@@ -47,6 +54,9 @@ struct DeviceState {
     Region regions[kMaxStreams];
     int nregions = 0;
     hipStream_t clear_stream = nullptr;  // library-private: clears the counters of new regions
+    // this device's copy of `scratch`, as a device address (from hipGetSymbolAddress: in host
+    // code the array's own name is not a device address)
+    uint32_t* scratch_ptr = nullptr;
 };
 
 std::mutex g_mu;
@@ -120,9 +130,10 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     return GEMM_OK;
 }
 
-// force: 0 dispatch on M, 1 skinny, 2 large-tile family; glu: the SwiGLU form
+// force: 0 dispatch on M, 1 skinny, 2 large-tile family; glu: the SwiGLU form; noalloc: split
+// partials and counters in the device's scratch array instead of the stream's region
 int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-        void* C, int64_t ldc, hipStream_t stream, int force, bool glu = false) {
+        void* C, int64_t ldc, hipStream_t stream, int force, bool glu = false, bool noalloc = false) {
     int st = validate(M, N, K, A, lda, B, ldb, C, ldc, glu);
     if (st != GEMM_OK) return st;
     if (force == 1 && (M < 1 || M > 64)) return GEMM_ERR_UNSUPPORTED;
@@ -140,9 +151,19 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
     // (no buffer that fits in device memory gets here; the launch takes a 32-bit grid)
     if (p.grid > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
     Region* rg = nullptr;
+    Region fixed;
     if (p.kernel == glk::kKernTile || p.kernel == glk::kKernSkinny) {
-        st = region_for(ds, stream, &rg);
-        if (st != GEMM_OK) return st;
+        if (noalloc) {
+            // the plan is gemm_bf16's own (same bits); one whose partials or counters do not fit
+            // the scratch array is refused rather than changed
+            if (p.ws_floats > kScratchFloats || p.counters > kScratchCounters) return GEMM_ERR_UNSUPPORTED;
+            fixed.counters = ds.scratch_ptr;
+            fixed.ws = reinterpret_cast<float*>(ds.scratch_ptr + kScratchCounters);
+            rg = &fixed;
+        } else {
+            st = region_for(ds, stream, &rg);
+            if (st != GEMM_OK) return st;
+        }
     }
     const uint16_t* a16 = static_cast<const uint16_t*>(A);
     const uint16_t* b16 = static_cast<const uint16_t*>(B);
@@ -412,6 +433,15 @@ int gemm_init(int device) {
             rc = GEMM_ERR_HIP;
         }
     }
+    // this device's copy of the scratch array: its address, and its counters cleared once here
+    // (the kernels return every counter they use to zero)
+    if (rc == GEMM_OK && hipGetSymbolAddress(reinterpret_cast<void**>(&ds.scratch_ptr), HIP_SYMBOL(scratch)) != hipSuccess) {
+        ds.scratch_ptr = nullptr;
+        rc = GEMM_ERR_HIP;
+    }
+    if (rc == GEMM_OK && (hipMemsetAsync(ds.scratch_ptr, 0, kScratchCounters * sizeof(uint32_t), ds.clear_stream) != hipSuccess ||
+                          hipStreamSynchronize(ds.clear_stream) != hipSuccess))
+        rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_skinny_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_tile_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
     if (rc == GEMM_OK && glk::configure_mx_kernels() != hipSuccess) rc = GEMM_ERR_HIP;
@@ -430,6 +460,11 @@ int gemm_init(int device) {
 int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
               int64_t ldb, void* C, int64_t ldc, gemm_stream_t stream) {
     return run(M, N, K, A, lda, B, ldb, C, ldc, reinterpret_cast<hipStream_t>(stream), 0);
+}
+
+int gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                      int64_t ldb, void* C, int64_t ldc, gemm_stream_t stream) {
+    return run(M, N, K, A, lda, B, ldb, C, ldc, reinterpret_cast<hipStream_t>(stream), 0, false, true);
 }
 
 int gemm_bf16_skinny(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
