@@ -17,10 +17,12 @@ prints the mean, minimum and maximum duration of the next K, and their span (fir
 last end) divided by K: e.g. the timed region of a benchmark that runs N warm-up launches
 first.
 `counters` averages every counter of one or more `--pmc` passes over the dispatches of the
-matching kernel and derives the busy fractions: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over
-(GRBM_GUI_ACTIVE x CUs x 4 SIMDs), wave wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, TA busy =
-TA_TA_BUSY over (GRBM_GUI_ACTIVE x CUs), TA address FIFO full = SQ_VMEM_TA_ADDR_FIFO_FULL over
-(GRBM_GUI_ACTIVE x CUs), and LDS bank conflicts per LDS instruction.
+matching kernel and derives the busy fractions. GRBM_GUI_ACTIVE is summed over the XCDs, so the
+kernel's cycles are G = GRBM_GUI_ACTIVE / XCDs; then MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over
+(G x CUs x 4 SIMDs), TA busy = TA_TA_BUSY over (G x CUs), TA address FIFO full =
+SQ_VMEM_TA_ADDR_FIFO_FULL over (G x CUs), LDS busy = SQ_LDS_IDX_ACTIVE over (G x CUs), the wave
+wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, LDS bank conflicts per LDS instruction, and the
+L2 hit rate TCC_HIT / (TCC_HIT + TCC_MISS).
 `traffic` turns two counter passes (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, both over a
 command that also runs the library's copy kernel on `--copy-bytes` bytes, e.g.
 `bench.py --copy-calibration`) into HBM bytes per launch of the kernel matching REGEX: each
@@ -176,9 +178,12 @@ def counter_means(paths, kernel_regex: str, grid: int = 0) -> tuple[dict, dict]:
     return {k: _mean(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
 
 
-def derived_fractions(m: dict, cus: int) -> dict:
+def derived_fractions(m: dict, cus: int, xcds: int = 8) -> dict:
     out = {}
     gui = m.get("GRBM_GUI_ACTIVE")
+    if gui:
+        gui = gui / xcds
+        out["kernel_cycles_per_xcd"] = gui
     if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
         out["mfma_busy_frac"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * cus * 4)
     if "SQ_WAIT_INST_ANY" in m and m.get("SQ_WAVE_CYCLES"):
@@ -191,6 +196,8 @@ def derived_fractions(m: dict, cus: int) -> dict:
         out["ta_addr_stalled_by_tc_frac"] = m["TA_ADDR_STALLED_BY_TC_CYCLES"] / (gui * cus)
     if gui and "SQ_VMEM_TA_ADDR_FIFO_FULL" in m:
         out["ta_addr_fifo_full_frac"] = m["SQ_VMEM_TA_ADDR_FIFO_FULL"] / (gui * cus)
+    if gui and "SQ_LDS_IDX_ACTIVE" in m:
+        out["lds_busy_frac"] = m["SQ_LDS_IDX_ACTIVE"] / (gui * cus)
     if m.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in m:
         out["lds_bank_conflict_cycles_per_lds_inst"] = m["SQ_LDS_BANK_CONFLICT"] / m["SQ_INSTS_LDS"]
     if m.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in m:
@@ -210,7 +217,7 @@ def cmd_counters(a) -> None:
             print(f"# command: {ln}")
     for k in sorted(means):
         print(f"{k}: {means[k]:.1f}   # {counts[k]} dispatches")
-    for k, v in derived_fractions(means, a.cus).items():
+    for k, v in derived_fractions(means, a.cus, a.xcds).items():
         print(f"{k}: {v:.4f}")
 
 
@@ -243,6 +250,7 @@ def main(argv=None) -> None:
     c.add_argument("--kernel", required=True)
     c.add_argument("--grid", type=int, default=0, help="only dispatches with this many threads")
     c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
     c.add_argument("--command", default="")
     a = ap.parse_args(argv)
     {"stats": cmd_stats, "traffic": cmd_traffic, "window": cmd_window, "counters": cmd_counters}[a.cmd](a)

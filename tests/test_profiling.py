@@ -109,7 +109,8 @@ def test_counters_average_per_dispatch_and_derive_fractions(tmp_path):
         [1, 131072, k, "SQ_WAVE_CYCLES", 400.0], [1, 131072, k, "SQ_WAIT_INST_ANY", 100.0],
         [2, 131072, k, "SQ_WAVE_CYCLES", 400.0], [2, 131072, k, "SQ_WAIT_INST_ANY", 300.0]])
     _write(p2, PMC_HEADER, [[5, 131072, k, "TA_TA_BUSY", 256000.0], [5, 131072, k, "GRBM_GUI_ACTIVE", 2000.0]])
-    kv = _kv(_run(["counters", str(p1), str(p2), "--kernel", "tile_gemm", "--grid", "131072", "--cus", "256"]))
+    kv = _kv(_run(["counters", str(p1), str(p2), "--kernel", "tile_gemm", "--grid", "131072", "--cus", "256",
+                   "--xcds", "1"]))
     assert float(kv["GRBM_GUI_ACTIVE"].split("#")[0]) == pytest.approx(2000.0)
     # 1024000 / (2000 * 256 * 4) = 0.5
     assert float(kv["mfma_busy_frac"]) == pytest.approx(0.5)
