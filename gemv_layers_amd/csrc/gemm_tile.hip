@@ -40,6 +40,8 @@
 //   epilogue combines them in registers (spark-kernels post, "the memory-bound kernels": SwiGLU
 //   in one kernel instead of two, here fused into the product that makes its inputs).
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -49,7 +51,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int SB_ = 3>
 struct TileTraits {
     static constexpr int BK = 32;                           // k per step (B stage, MFMA step)
     static constexpr int AK = 64;                           // k per A stage: 128-byte rows
@@ -57,7 +59,7 @@ struct TileTraits {
     // 72 KB for 128 x 128). A 3-stage B ring measured faster than 4 stages, with the same bits:
     // about 10% on every 128 x 128 grid and 0.5-1% with 256 x 256 tiles; 2 stages lost 25-30%
     static constexpr int SA = 3;
-    static constexpr int SB = 3;
+    static constexpr int SB = SB_;
     static constexpr int DB = SB;                           // steps B is issued ahead
     static constexpr int DA = DB + 1;                       // A half stages issued ahead
     static constexpr int NW = WM * WN;
@@ -378,10 +380,218 @@ tile_gemm_kernel(TileArgs p) {
     }
 }
 
+// ---- 256 x 256 tile, two wave groups alternating MFMA and memory phases ----------------------
+// The same tile, staging, swizzles, fragment layout and epilogue as tile_gemm_kernel<256, 256, 2,
+// 4>, with a different schedule for the eight waves. The waves form two groups of four, one wave
+// of each group per SIMD (group 0: waves 0-3, rows 0-127 of the tile; group 1: waves 4-7, rows
+// 128-255). Every 32-k step a wave runs two phases, separated by workgroup barriers:
+//   memory phase:  its MFMA operands for the step, LDS -> registers, and its share of the
+//                  direct-to-LDS loads of a later stage; then it waits for both;
+//   compute phase: the step's 32 MFMAs back to back, on operands already in registers.
+// Group 1 starts one barrier later, so while one group's four waves keep the four SIMDs' matrix
+// cores busy, the other group's waves fetch, and the roles swap at every barrier. (spark-kernels
+// post, "the copies were the problem, not the power": keep copies and their waits out of the
+// matrix instructions' stream; here the copies move to the other wave of each SIMD, not to a
+// dedicated producer, because gfx950 gives every wave of a workgroup the same register budget.)
+//
+// Barriers after the prologue's are numbered b1, b2, ...; group 0 runs the memory phase of step
+// s before b(2s+1) and its compute phase before b(2s+2); group 1 (with its extra first barrier)
+// one barrier later. The last LDS read of step s's data is group 1's, before b(2s+2); so B stage
+// s + SB - 1, which reuses step s - 1's slot, and A half stage s + 4, which reuses a slot last read
+// before b(2s), may be issued in step s's memory phases. Each wave waits at the end of its memory
+// phase of step s for its loads of step s + 1 (issued by iteration s + 1 - DB and earlier), before
+// the barrier after which group 0 reads them.
+template <int SB, bool GLU>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+tile_pp_kernel(TileArgs p) {
+    constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
+    using T = TileTraits<BM, BN, WM, WN, SB>;
+    static_assert(T::TN % 2 == 0, "SwiGLU pairs gate and up tiles within a wave");
+    static_assert(T::LDS_BYTES <= 160 * 1024, "LDS");
+    constexpr int BK = T::BK, TM = T::TM, TN = T::TN;
+    constexpr int DB = SB - 1;  // B stages issued ahead
+    constexpr int DA = 4;       // A half stages issued ahead
+    constexpr int LOADS = T::LOADS;
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int wm = grp, wn = wave & 3;
+
+    // ---- which tile (data-parallel only) -------------------------------------------------------
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const int tile = xcd_remap((int)blockIdx.x, ntiles, p.nxcd);
+    const int per_group = p.group_m * p.tiles_n;
+    const int g = tile / per_group;
+    const int first_m = g * p.group_m;
+    const int gm = min(p.tiles_m - first_m, p.group_m);
+    const int in_g = tile - g * per_group;
+    const int tm = first_m + in_g % gm;
+    const int tn = in_g / gm;
+    const int m0 = tm * BM, n0 = tn * (GLU ? BN / 2 : BN);
+    const int nsteps = (p.K + BK - 1) / BK;
+
+    // ---- direct-to-LDS load addressing (as in tile_gemm_kernel) ------------------------------
+    uint32_t a_off[T::A_PER_WAVE];
+    int a_kchunk[T::A_PER_WAVE];
+    bool a_row_ok[T::A_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < T::A_PER_WAVE; ++i) {
+        const int row = 8 * (wave * T::A_PER_WAVE + i) + (lane >> 3);
+        a_kchunk[i] = a_swz(lane & 7, row);
+        a_row_ok[i] = m0 + row < p.M;
+        a_off[i] = (uint32_t)(row * p.lda + 8 * a_kchunk[i]) * 2u;
+    }
+    uint32_t b_off[T::B_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < T::B_PER_WAVE; ++i) {
+        const int k = (wave * T::B_PER_WAVE + i) * T::B_ROWS_PER_INSTR + lane / T::B_CHUNKS;
+        const int pc = lane % T::B_CHUNKS;
+        const int col = 16 * b_swz(pc >> 1, k) + 8 * (pc & 1);
+        if constexpr (GLU) {
+            const int r = col % T::WTN;
+            const int out = (col / T::WTN) * (T::WTN / 2) + r % (T::WTN / 2);
+            const int src = (r < T::WTN / 2 ? 0 : p.N) + out;
+            b_off[i] = sel_off(n0 + out < p.N, (uint32_t)(k * p.ldb + src) * 2u);
+        } else {
+            b_off[i] = sel_off(n0 + col < p.N, (uint32_t)(k * p.ldb + col) * 2u);
+        }
+    }
+    // half H (a compile-time 0 or 1) of A stage st
+    auto issue_a_half = [&](int st, auto hc) {
+        constexpr int H = decltype(hc)::value;
+        const uint32_t st_lds = lds_addr(lds + (st % T::SA) * T::A_BYTES);
+        const int k0 = st * T::AK;
+        const int krows = max(0, min(T::AK, p.K - k0));  // uniform
+        const i32x4 ar = rsrc_words(p.A + (size_t)m0 * p.lda + k0, kBufRecords);
+#pragma unroll
+        for (int u = 0; u < T::A_HALF; ++u) {
+            const int t = H * T::A_HALF + u;
+            const bool ok = a_row_ok[t] & (8 * a_kchunk[t] < krows);
+            dma16(ar, st_lds + (wave * T::A_PER_WAVE + t) * 1024, sel_off(ok, a_off[t]));
+        }
+    };
+    auto issue_b = [&](int i) {
+        const uint32_t st_lds = lds_addr(lds + T::B_RING + (i % SB) * T::B_BYTES);
+        const int k0 = i * BK;
+        const int krows = (i < nsteps) ? min(BK, p.K - k0) : 0;  // uniform
+        const i32x4 br = rsrc_words(p.B + (size_t)k0 * p.ldb + n0, (uint32_t)krows * (uint32_t)p.ldb * 2u);
+#pragma unroll
+        for (int t = 0; t < T::B_PER_WAVE; ++t)
+            dma16(br, st_lds + (wave * T::B_PER_WAVE + t) * 1024, b_off[t]);
+    };
+
+    f32x4 acc[TN][TM];
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi) acc[ni][mi] = f32x4{};
+
+    const int fa_row = lane & 15, fG = lane >> 4, fj = lane & 15;
+    const int fb_k = 8 * fG + (fj >> 2);
+    const int fb_n = 4 * (fj & 3);
+    bf16x8 fa[TM], fb[TN];
+    auto read_frags = [&](int i) {
+        const char* sa = lds + ((i >> 1) % T::SA) * T::A_BYTES;
+        const char* sb = lds + T::B_RING + (i % SB) * T::B_BYTES;
+        const int ch = 4 * (i & 1) + fG;
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi) {
+            const int m = wm * T::WTM + mi * 16 + fa_row;
+            fa[mi] = *reinterpret_cast<const bf16x8*>(sa + m * 128 + 16 * a_swz(ch, m));
+        }
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni) {
+            const int n = wn * T::WTN + ni * 16 + fb_n;
+            i16x4 v[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = fb_k + 4 * h;
+                const char* addr = sb + k * (2 * BN) + 32 * b_swz(n >> 4, k) + 2 * (n & 15);
+                v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)addr);
+            }
+            const i16x8 x = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+            fb[ni] = __builtin_bit_cast(bf16x8, x);
+        }
+    };
+    auto phase_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: the loads iterations -DA .. -1 would issue; step 0's data landed ----------
+    // (iteration I issues A half stage I + DA, then B stage I + DB; in the loop the wait for step
+    // s + 1's data then allows exactly the last DB - 1 iterations' loads in flight)
+    static_assert(DA == 4 && DB >= 2 && DB <= 3, "load order and counts");
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    issue_a_half(0, H0{});   // iteration -4
+    issue_a_half(0, H1{});   // iteration -3
+    if (DB >= 3) issue_b(0);
+    issue_a_half(1, H0{});   // iteration -2
+    issue_b(DB - 2);
+    issue_a_half(1, H1{});   // iteration -1
+    issue_b(DB - 1);
+    wait_vmcnt<LOADS * (DB - 1)>();
+    lds_barrier();
+    if (grp == 1) phase_barrier();
+    // step s issues A half stage s + DA (half (s + DA) & 1 = s & 1) and B stage s + DB
+    auto step = [&](int s, auto hc) {
+        // memory phase
+        read_frags(s);
+        issue_a_half((s + DA) >> 1, hc);
+        issue_b(s + DB);
+        wait_vmcnt<LOADS * (DB - 1)>();  // this wave's loads for step s + 1 landed
+        wait_lgkmcnt0();                 // and its operands for step s are in registers
+        phase_barrier();
+        // compute phase
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+            for (int mi = 0; mi < TM; ++mi) acc[ni][mi] = mfma16(fb[ni], fa[mi], acc[ni][mi]);
+        phase_barrier();
+    };
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+        step(s, H0{});
+        step(s + 1, H1{});
+    }
+    if (s < nsteps) step(s, H0{});
+    if (grp == 0) phase_barrier();
+    wait_vmcnt<0>();  // no direct-to-LDS write may outlive the workgroup
+
+    // ---- epilogue: bf16 (round to nearest even), 8-byte stores ------------------------------
+    constexpr int TNO = GLU ? TN / 2 : TN;
+    constexpr int WTNO = GLU ? T::WTN / 2 : T::WTN;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + (size_t)m0 * p.ldc + n0);
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+        const int m = wm * T::WTM + mi * 16 + fa_row;
+        const bool m_ok = (m0 + m) < p.M;
+#pragma unroll
+        for (int ni = 0; ni < TNO; ++ni) {
+            const int n = wn * WTNO + ni * 16 + 4 * fG;
+            const bool ok = m_ok && (n0 + n) < p.N;
+            f32x4 h;
+            if constexpr (GLU) {
+                h = swiglu4(acc[ni][mi], acc[ni + TNO][mi]);
+            } else {
+                h = acc[ni][mi];
+            }
+            u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+            buf_store8(rc, ok ? (uint32_t)(m * p.ldc + n) * 2u : kBufInvalid, v);
+        }
+    }
+}
+
 TileShape tile_shape(int cfg) {
     switch (cfg) {
         case kTile256x256w8: return {256, 256, 32, 512};
         case kTile128x128w4: return {128, 128, 32, 256};
+        case kTile256x256pp: return {256, 256, 32, 512};
         default: return {0, 0, 0, 0};
     }
 }
@@ -395,6 +605,28 @@ static hipError_t launch_cfg(const TileArgs& a, int grid, bool glu, hipStream_t 
     else
         tile_gemm_kernel<BM, BN, WM, WN, false><<<grid, T::NT, T::LDS_BYTES, s>>>(a);
     return hipGetLastError();
+}
+
+template <int SB>
+static hipError_t launch_pp(const TileArgs& a, int grid, bool glu, hipStream_t s) {
+    using T = TileTraits<256, 256, 2, 4, SB>;
+    if (a.sched != kSchedDataParallel) return hipErrorInvalidValue;
+    if (glu)
+        tile_pp_kernel<SB, true><<<grid, T::NT, T::LDS_BYTES, s>>>(a);
+    else
+        tile_pp_kernel<SB, false><<<grid, T::NT, T::LDS_BYTES, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int SB>
+static hipError_t configure_pp() {
+    const int bytes = TileTraits<256, 256, 2, 4, SB>::LDS_BYTES;
+    hipError_t e = hipFuncSetAttribute((const void*)tile_pp_kernel<SB, false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)tile_pp_kernel<SB, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return e;
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -412,6 +644,7 @@ static hipError_t configure_cfg() {
 hipError_t configure_tile_kernels() {
     hipError_t e = configure_cfg<256, 256, 2, 4>();
     if (e == hipSuccess) e = configure_cfg<128, 128, 2, 2>();
+    if (e == hipSuccess) e = configure_pp<4>();
     return e;
 }
 
@@ -419,6 +652,7 @@ hipError_t launch_tile_gemm(int cfg, const TileArgs& a, int grid, bool glu, hipS
     switch (cfg) {
         case kTile256x256w8: return launch_cfg<256, 256, 2, 4>(a, grid, glu, s);
         case kTile128x128w4: return launch_cfg<128, 128, 2, 2>(a, grid, glu, s);
+        case kTile256x256pp: return launch_pp<4>(a, grid, glu, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -33,8 +33,9 @@ struct TileArgs {
 
 // Tile configurations compiled into the library.
 enum TileConfig : int {
-    kTile256x256w8 = 0,  // 256 x 256 tile, 8 waves of 128 x 64
+    kTile256x256w8 = 0,  // 256 x 256 tile, 8 waves of 128 x 64, all in step (kept for comparison)
     kTile128x128w4 = 1,  // 128 x 128 tile, 4 waves of 64 x 64
+    kTile256x256pp = 2,  // 256 x 256 tile, 8 waves in two groups alternating MFMA and memory phases
     kTileConfigCount
 };
 
