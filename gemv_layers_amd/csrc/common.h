@@ -24,11 +24,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
                                              kBufWord3);
 }
 
-// Descriptor with an explicit byte range: offsets at or beyond `bytes` read as zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
-}
-
 // `off` when `valid`, else an out-of-range offset; branch-free so that no control flow (and no
 // conservative wait at a merge point) ends up between a wave's outstanding loads.
 __device__ __forceinline__ uint32_t sel_off(bool valid, uint32_t off) {
@@ -54,6 +49,8 @@ __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t o
 // them to complete, workgroup barrier, one device-scope counter increment. No cache-wide
 // write-back or invalidate is needed.
 constexpr int kAuxDevice = 16;
+// Non-temporal (streaming) stores: data written once and not read back by this kernel.
+constexpr int kAuxNonTemporal = 2;
 
 __device__ __forceinline__ void buf_store16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kAuxDevice);
@@ -149,22 +146,6 @@ __device__ __forceinline__ f32x4 swiglu4(f32x4 g, f32x4 u) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
-
-// Transpose of an 8 x 8 block of 16-bit values held as 8 rows of 4 dwords (row r, dword q holds
-// columns 2q (low half) and 2q+1 (high half)). Output column c as 4 dwords, dword p holding rows
-// 2p (low half) and 2p+1 (high half).
-__device__ __forceinline__ void transpose8x8_b16(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t x = in[2 * p][q], y = in[2 * p + 1][q];
-            // even column 2q: low halves of rows 2p, 2p+1; odd column 2q+1: high halves
-            out[2 * q][p] = __builtin_amdgcn_perm(y, x, 0x05040100u);
-            out[2 * q + 1][p] = __builtin_amdgcn_perm(y, x, 0x07060302u);
-        }
-    }
-}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -561,31 +561,57 @@ tile_pp_kernel(TileArgs p) {
     }
     if (s < nsteps) step(s, H0{});
     if (grp == 0) phase_barrier();
-    wait_vmcnt<0>();  // no direct-to-LDS write may outlive the workgroup
+    wait_vmcnt<0>();  // every direct-to-LDS write of this wave (prefetches past K included) landed
+    lds_barrier();    // ... and of every wave: the ring is free for the output
 
-    // ---- epilogue: bf16 (round to nearest even), 8-byte stores ------------------------------
+    // ---- epilogue: bf16 (round to nearest even) through LDS, whole 128-byte rows ------------
+    // Lane l holds rows 16 mi + (l & 15), columns 16 ni + 4 (l >> 4) .. + 3 of the wave's tile,
+    // 8 bytes per (mi, ni) once rounded. Each wave writes its WTM x WTNO bf16 block to its own
+    // LDS area (rows of RB bytes, 16-byte chunk c of row r stored at c ^ (r & 7)), then reads it
+    // back 16 bytes per lane, RB / 16 lanes per row, and writes C in whole row segments: one
+    // 16-byte store per lane instead of two 8-byte ones, every row segment written by one
+    // instruction (measured: the 8-byte stores took 6.5 us of a 103 us 4096^3 product; this
+    // epilogue takes about 4 us, and 101 us for the whole product).
+    // (SwiGLU: gate tile ni and up tile ni + TN / 2 hold the same outputs)
     constexpr int TNO = GLU ? TN / 2 : TN;
     constexpr int WTNO = GLU ? T::WTN / 2 : T::WTN;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + (size_t)m0 * p.ldc + n0);
+    constexpr int RB = WTNO * 2;                 // bytes per output row of the wave's block
+    constexpr int CPR = RB / 16;                 // 16-byte chunks per row (8 or 4)
+    constexpr int ROWS_PER_ST = 64 / CPR;        // rows per 16-byte store instruction
+    static_assert(T::WTM * RB * 8 <= T::LDS_BYTES, "output blocks fit the ring");
+    char* ob = lds + wave * (T::WTM * RB);
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
-        const int m = wm * T::WTM + mi * 16 + fa_row;
-        const bool m_ok = (m0 + m) < p.M;
+        const int r = mi * 16 + fa_row;
 #pragma unroll
         for (int ni = 0; ni < TNO; ++ni) {
-            const int n = wn * WTNO + ni * 16 + 4 * fG;
-            const bool ok = m_ok && (n0 + n) < p.N;
             f32x4 h;
             if constexpr (GLU) {
                 h = swiglu4(acc[ni][mi], acc[ni + TNO][mi]);
             } else {
                 h = acc[ni][mi];
             }
-            u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-            buf_store8(rc, ok ? (uint32_t)(m * p.ldc + n) * 2u : kBufInvalid, v);
+            const u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+            const int byte = ni * 32 + fG * 8;         // within the row
+            const int c = (byte >> 4) ^ (r & (CPR - 1) & 7);
+            *reinterpret_cast<u32x2*>(ob + r * RB + c * 16 + (byte & 15)) = v;
         }
     }
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + (size_t)m0 * p.ldc + n0);
+    const int lr = lane / CPR, lc = lane % CPR;  // row within a store, logical chunk
+    const int gn = wn * WTNO + lc * 8;           // output column of the chunk, within the tile
+#pragma unroll
+    for (int st = 0; st < T::WTM / ROWS_PER_ST; ++st) {
+        const int r = st * ROWS_PER_ST + lr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ob + r * RB + (lc ^ (r & (CPR - 1) & 7)) * 16);
+        const int m = wm * T::WTM + r;
+        const bool ok = (m0 + m) < p.M && (n0 + gn) < p.N;
+        // non-temporal: C is written once and is far larger than the L2s (measured 1.2-1.4%
+        // faster on multi-wave grids, neutral at 4096^3)
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? (uint32_t)(m * p.ldc + gn) * 2u : kBufInvalid, 0, kAuxNonTemporal);
+    }
 }
+
 
 TileShape tile_shape(int cfg) {
     switch (cfg) {
