@@ -275,8 +275,10 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
         return last_flag != 0;
     };
     // the last arriver: every piece, added in K order (all loads of a batch issued before any
-    // add), written as bf16; the counter goes back to zero for the next launch
-    auto reduce = [&](int strip) {
+    // add), written as bf16; the counter goes back to zero for the next launch. With own_in_acc
+    // this workgroup's own piece is still in acc (the strip its range ends in) and is not read
+    // back: the stored copy holds the same bits.
+    auto reduce = [&](int strip, bool own_in_acc) {
         int wf, wl;
         pieces_of(strip, wf, wl);
         if (tid == 0) counter_reset(&p.counters[strip]);
@@ -295,21 +297,25 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
             for (int q = 0; q < PB; ++q) {
                 const int wg = b0 + q;
                 const int sq = (wg == wf) ? seg_first : 0;
+                const bool own = own_in_acc && wg == w;
 #pragma unroll
                 for (int t = 0; t < TN; ++t)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
-                        const uint32_t off = sel_off(wg <= wl && 16 * mt + part_row < p.M, slot_off(wg, sq, t, mt));
+                        const uint32_t off = sel_off(!own && wg <= wl && 16 * mt + part_row < p.M, slot_off(wg, sq, t, mt));
                         v[q][t][mt] = bits_f4(buf_load16_dev(ws, off));
                     }
             }
-            // pieces past wl read as zeros (out-of-range offsets), so adding them changes nothing
+            // pieces past wl read as zeros (out-of-range offsets), so adding them changes nothing;
+            // the own piece (read as zeros above) comes from the registers, at its place in K order
 #pragma unroll
-            for (int q = 0; q < PB; ++q)
+            for (int q = 0; q < PB; ++q) {
+                const bool own = own_in_acc && b0 + q == w;
 #pragma unroll
                 for (int t = 0; t < TN; ++t)
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) sum[t][mt] += v[q][t][mt];
+                    for (int mt = 0; mt < MT; ++mt) sum[t][mt] += own ? acc[t][mt] : v[q][t][mt];
+            }
         }
 #pragma unroll
         for (int t = 0; t < TN; ++t)
@@ -360,17 +366,19 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
                     pend_at = i + STAGES;
                 }
             }
+            if (i < nunits - 1) {  // (after the range's last unit acc keeps the piece for reduce)
 #pragma unroll
-            for (int t = 0; t < TN; ++t)
+                for (int t = 0; t < TN; ++t)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{};
+                    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{};
+            }
         }
     }
     wait_vmcnt<0>();  // every load and partial store of this wave has completed
     if (pend >= 0 && arrive(pend)) red0 = pend;
     if (fin >= 0 && arrive(fin)) red1 = fin;
-    if (red0 >= 0) reduce(red0);
-    if (red1 >= 0) reduce(red1);
+    if (red1 >= 0) reduce(red1, true);  // first, while acc still holds this range's last piece
+    if (red0 >= 0) reduce(red0, false);
 }
 
 template <int MT, int SW>
