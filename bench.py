@@ -133,6 +133,7 @@ def parse():
                     help="skip the compute-bound workloads other than the headline")
     ap.add_argument("--only", default="", help="comma-separated compute workloads to time (default: all)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
+    ap.add_argument("--decode", default="", help="comma-separated decode workloads to time (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-torch", action="store_true", help="skip the torch.matmul comparison")
@@ -309,7 +310,11 @@ def main():
         while time.time() < t_end:
             mfma_run(20000)
         burst = max(mfma_run(20000)[0] for _ in range(3))
-        sus_tf, sus_ms, sus_clk = mfma_run(5_000_000)
+        sampler = PowerSampler()
+        with sampler:
+            sus_tf, sus_ms, sus_clk = mfma_run(5_000_000)
+        watts = [x[1] for x in sampler.samples[1:] if x[1] is not None]
+        peaks["mfma_sustained_power_w_median"] = round(float(np.median(watts)), 1) if watts else None
         peaks["mfma_bf16_fp32_tflops_burst"] = round(burst, 1)
         peaks["mfma_bf16_fp32_tflops_sustained"] = round(sus_tf, 1)
         peaks["mfma_sustained_ms"] = round(sus_ms, 1)
@@ -485,7 +490,8 @@ def main():
         dec = {}
         copies = 12
         shapes = {}
-        for name in sorted(n for n in WORKLOADS if n.startswith("dec_")):
+        for name in sorted(n for n in WORKLOADS if n.startswith("dec_")
+                           and (not args.decode or n in args.decode.split(","))):
             wd = WORKLOADS[name]
             key = (wd.K, wd.N)
             if key not in shapes:
