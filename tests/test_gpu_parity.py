@@ -540,3 +540,36 @@ def test_workgroups_are_dealt_to_xcds_round_robin():
     assert nxcd == len(set(x.tolist())), f"planner nxcd {nxcd}, probe saw XCDs {sorted(set(x.tolist()))}"
     assert len(set(x[:nxcd].tolist())) == nxcd
     assert np.array_equal(x, np.tile(x[:nxcd], blocks // nxcd)), "workgroups not dealt round robin"
+
+
+def test_tile_schedules_give_the_same_bits():
+    # the two-group schedule and the all-waves-in-step schedule feed every accumulator the same
+    # MFMAs in the same K order, so their outputs must agree bit for bit; the older schedule is
+    # selected in a child process through the planner's debug override
+    import os
+    import subprocess
+    import sys
+    M, N, K = 777, 6704, 1000
+    A = matrix("normal", M, K, seed=31000)
+    B = matrix("normal", K, N, seed=32000, sigma=0.5)
+    mine = run("tiled", A, B, M, N, K)
+    assert g.gemm_last_plan()["bm"] == 256
+    code = f"""
+import ctypes, sys, numpy as np, torch
+sys.path.insert(0, {os.path.dirname(os.path.dirname(os.path.abspath(__file__)))!r})
+import gemv_layers_amd as g
+from synth import matrix
+torch.cuda.set_device(0); g.gemm_init(0)
+A = matrix("normal", {M}, {K}, seed=31000); B = matrix("normal", {K}, {N}, seed=32000, sigma=0.5)
+dA = torch.from_numpy(A.view(np.int16)).cuda(); dB = torch.from_numpy(B.view(np.int16)).cuda()
+C = torch.empty({M} * {N}, dtype=torch.bfloat16, device="cuda")
+g.gemm_bf16_tiled({M}, {N}, {K}, ctypes.c_void_p(dA.data_ptr()), {K}, ctypes.c_void_p(dB.data_ptr()), {N},
+                  ctypes.c_void_p(C.data_ptr()), {N}, g.current_stream_handle())
+torch.cuda.synchronize()
+sys.stdout.buffer.write(C.cpu().view(torch.int16).numpy().tobytes())
+"""
+    env = dict(os.environ, GEMM_BF16_FORCE_TILE="0")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, timeout=240)
+    assert r.returncode == 0, r.stderr.decode()[-2000:]
+    other = np.frombuffer(r.stdout, dtype=np.uint16).reshape(M, N)
+    assert np.array_equal(mine, other)
