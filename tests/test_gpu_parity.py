@@ -573,3 +573,52 @@ sys.stdout.buffer.write(C.cpu().view(torch.int16).numpy().tobytes())
     assert r.returncode == 0, r.stderr.decode()[-2000:]
     other = np.frombuffer(r.stdout, dtype=np.uint16).reshape(M, N)
     assert np.array_equal(mine, other)
+
+
+# ---- every element at full size ----------------------------------------------------------------
+# Integer inputs make the exact result the expected bits (see above); for the workloads the host
+# oracle finishes in seconds, every element is compared, not a row sample. 16384^3 (8.8 TFLOP in
+# float64) is checked on every element against a closed form instead.
+
+@pytest.mark.parametrize("name", ["sq512", "sq4096", "mlp_up", "mlp_down", "sq8192"] +
+                         [n for n in WORKLOADS if n.startswith("dec_")])
+def test_workload_integer_exact_every_element(name):
+    w = WORKLOADS[name]
+    A = matrix("int", w.M, w.K, seed=w.seed_a + 0x100)
+    B = matrix("int", w.K, w.N, seed=w.seed_b + 0x100)
+    C = run("auto", A, B, w.M, w.N, w.K)
+    ref, _ = oracle.gemm(A, B, with_abs=False)
+    want = oracle.bf16_rne(ref)
+    bad = np.count_nonzero(C != want)
+    assert bad == 0, f"{name}: {bad} of {C.size} elements differ"
+
+
+def test_sq16384_rank_one_closed_form_every_element():
+    # A[i][k] = a_i x_k and B[k][j] = y_k b_j with small integers: C[i][j] = a_i b_j (x . y), a
+    # value that depends on the row and the column, so a misplaced row, column or k slice shows.
+    # x . y = 2^10 and a_i b_j <= 15: every result and partial sum (|.| <= 15 K < 2^24) is exact
+    # in float32 and in bf16.
+    n = 16384
+    i = np.arange(n)
+    a = (1 + (i * 7) % 5).astype(np.float32)            # 1 .. 5
+    b = (1 + (i * 11) % 3).astype(np.float32)           # 1 .. 3
+    x = np.where(i % 3 == 0, 1.0, np.where(i % 3 == 1, -1.0, 0.0)).astype(np.float32)
+    y = np.where(i % 3 == 0, 1.0, np.where(i % 3 == 1, 1.0, 0.0)).astype(np.float32)
+    # make x . y exactly 2^10: zero every contribution past the first 1024 + 1024 matched pairs
+    ones = np.flatnonzero(i % 3 == 0)[:1024 + 1024]
+    negs = np.flatnonzero(i % 3 == 1)[:1024]
+    x[:] = 0.0
+    y[:] = 0.0
+    x[ones] = 1.0
+    y[ones] = 1.0
+    x[negs] = -1.0
+    y[negs] = 1.0
+    s = float(x.astype(np.float64) @ y.astype(np.float64))
+    assert s == 1024.0
+    from synth import f32_to_bf16_bits
+    A = f32_to_bf16_bits(np.outer(a, x).astype(np.float32))
+    B = f32_to_bf16_bits(np.outer(y, b).astype(np.float32))
+    C = run("auto", A, B, n, n, n)
+    want = f32_to_bf16_bits((np.outer(a, b) * s).astype(np.float32))
+    bad = np.count_nonzero(C != want)
+    assert bad == 0, f"{bad} of {C.size} elements differ from a_i b_j (x . y)"
