@@ -62,14 +62,18 @@ struct SkinnyTraits {
     static constexpr int CHUNKS = ROW_BYTES / 16;          // 16-byte chunks per B row
     static constexpr int A_BYTES = 16 * MT * kSkRows * 2;  // A rows (M padded to 16 MT) x 64 k
     static constexpr int STAGE_BYTES = B_BYTES + A_BYTES;
-    // ring for 128-column strips: 80 KB (4 stages) for one or two 16-row tiles of M, 96 KB (4
-    // stages) above that; measured with settled clocks against the earlier 128 KB, same bits:
-    // dec_down_M1 22.3 -> 20.4 us, dec_down_M16 22.7 -> 21.0, dec_up_M64 29.3 -> 28.4. All of LDS
-    // (less the padding sink and the static flag) for 256-column strips, whose stages are twice
-    // as big
+    // ring: 4 stages in every configuration. 128-column strips: 72, 80, 88 and 96 KB for one to
+    // four 16-row tiles of M (budgets of 80 KB up to two tiles, 96 KB above; measured with
+    // settled clocks against the earlier 128 KB, same bits: dec_down_M1 22.3 -> 20.4 us,
+    // dec_down_M16 22.7 -> 21.0, dec_up_M64 29.3 -> 28.4). 256-column strips: 136 and 144 KB
+    // (all of LDS less the padding sink and the static flag; their stages are twice as big)
     static constexpr int STAGES = (SW == 128 ? (MT <= 2 ? 81920 : 98304) : 163840 - 2048) / STAGE_BYTES;
     static constexpr int DUMMY = STAGES * STAGE_BYTES;     // 1 KB sink for padding loads
     static constexpr int LDS_BYTES = DUMMY + 1024;
+    // LDS the launch asks for: more than half of a CU's 160 KB, so no two workgroups ever share a
+    // CU (the grids are sized to one workgroup per CU, and a second one would halve both's share
+    // of the CU's load path)
+    static constexpr int LAUNCH_LDS = LDS_BYTES > 81920 ? LDS_BYTES : 81920 + 1024;
     static constexpr int A_INSTR = A_BYTES / 1024;         // 1 KB load instructions for A per stage
     static constexpr int A_PER_WAVE = (A_INSTR + 3) / 4;
     static constexpr int LOADS = B_PER_WAVE + A_PER_WAVE;  // load instructions per wave per stage
@@ -77,6 +81,7 @@ struct SkinnyTraits {
     static_assert(SW == 128 || SW == 256, "strip width");
     static_assert(B_PER_WAVE * ROWS_PER_INSTR == 16, "each wave loads 16 B rows of a stage");
     static_assert(STAGES >= 3, "need at least three stages");
+    static_assert(LAUNCH_LDS > 163840 / 2 && LAUNCH_LDS <= 163840, "one workgroup per CU");
     static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
 };
 
@@ -384,10 +389,10 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
 template <int MT, int SW>
 static hipError_t configure_one() {
     hipError_t e = hipFuncSetAttribute((const void*)skinny_gemm_kernel<MT, SW, false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<MT, SW>::LDS_BYTES);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<MT, SW>::LAUNCH_LDS);
     if (e == hipSuccess)
         e = hipFuncSetAttribute((const void*)skinny_gemm_kernel<MT, SW, true>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<MT, SW>::LDS_BYTES);
+                                hipFuncAttributeMaxDynamicSharedMemorySize, SkinnyTraits<MT, SW>::LAUNCH_LDS);
     return e;
 }
 hipError_t configure_skinny_kernels() {
@@ -412,10 +417,10 @@ template <int SW, bool GLU>
 static hipError_t launch_sw(int mtiles, const SkinnyArgs& a, hipStream_t s) {
     const int grid = a.grid;
     switch (mtiles) {
-        case 1: skinny_gemm_kernel<1, SW, GLU><<<grid, 256, SkinnyTraits<1, SW>::LDS_BYTES, s>>>(a); break;
-        case 2: skinny_gemm_kernel<2, SW, GLU><<<grid, 256, SkinnyTraits<2, SW>::LDS_BYTES, s>>>(a); break;
-        case 3: skinny_gemm_kernel<3, SW, GLU><<<grid, 256, SkinnyTraits<3, SW>::LDS_BYTES, s>>>(a); break;
-        case 4: skinny_gemm_kernel<4, SW, GLU><<<grid, 256, SkinnyTraits<4, SW>::LDS_BYTES, s>>>(a); break;
+        case 1: skinny_gemm_kernel<1, SW, GLU><<<grid, 256, SkinnyTraits<1, SW>::LAUNCH_LDS, s>>>(a); break;
+        case 2: skinny_gemm_kernel<2, SW, GLU><<<grid, 256, SkinnyTraits<2, SW>::LAUNCH_LDS, s>>>(a); break;
+        case 3: skinny_gemm_kernel<3, SW, GLU><<<grid, 256, SkinnyTraits<3, SW>::LAUNCH_LDS, s>>>(a); break;
+        case 4: skinny_gemm_kernel<4, SW, GLU><<<grid, 256, SkinnyTraits<4, SW>::LAUNCH_LDS, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -94,7 +94,7 @@ static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, 
     p.mtiles = (int)cdiv(M, 16);
     p.threads = 256;
     p.ks = (int)cdiv(K, kSkinnyStage);
-    // one workgroup per CU at most (the LDS ring takes 128 KB or more)
+    // one workgroup per CU at most: every launch asks for more than half of a CU's LDS
     p.slots = dev.cus;
     skinny_layout(N, p.ks, p.mtiles, dev.cus, glu, &p.strip, &p.grid);
     p.strips = (int)cdiv(N, p.strip);
