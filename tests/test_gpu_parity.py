@@ -624,3 +624,55 @@ def test_sq16384_rank_one_closed_form_every_element():
     want = f32_to_bf16_bits((np.outer(a, b) * s).astype(np.float32))
     bad = np.count_nonzero(C != want)
     assert bad == 0, f"{bad} of {C.size} elements differ from a_i b_j (x . y)"
+
+
+# ---- seeded random shapes across every dispatch regime ---------------------------------------
+
+def _random_cases(n, seed=20251202):
+    """(entry, M, N, K, lda, ldb, ldc) drawn from a fixed seed: M in the skinny, small-tile and
+    large-tile ranges; N and K multiples of 8 with padded leading dimensions (the fast kernels)
+    or arbitrary (the general kernel); at most 1.5e9 multiply-adds so the oracle takes a moment."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        regime = rng.choice(3, p=[0.4, 0.3, 0.3])
+        M = int(rng.integers(1, 65) if regime == 0 else rng.integers(65, 400) if regime == 1
+                else rng.integers(400, 1300))
+        fast = rng.random() < 0.75
+        N, K = int(rng.integers(1, 3000)), int(rng.integers(1, 2100))
+        if fast:
+            N, K = max(8, N - N % 8), max(8, K - K % 8)
+            pads = [0, 0, 8, 64]
+        else:
+            pads = [0, 1, 3, 13]
+        if M * N * K > 1.5e9:
+            continue
+        lda, ldb, ldc = (d + int(rng.choice(pads)) for d in (K, N, N))
+        entry = rng.choice(["auto", "auto", "tiled"] + (["skinny"] if M <= 64 else []))
+        cases.append((str(entry), M, N, K, lda, ldb, ldc))
+    return cases
+
+
+RANDOM_CASES = _random_cases(48)
+
+
+def test_random_cases_reach_every_kernel_family():
+    """The drawn cases cover the skinny, large-tile and general kernels (the dispatch rule,
+    checked on the host)."""
+    kinds = set()
+    for entry, M, N, K, lda, ldb, ldc in RANDOM_CASES:
+        fast = all(x % 8 == 0 for x in (N, K, lda, ldb, ldc))
+        kinds.add("generic" if not fast else "skinny" if (entry == "skinny" or (entry == "auto" and M <= 64)) else "tile")
+    assert kinds == {"generic", "skinny", "tile"}
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_CASES)))
+def test_random_shapes_integer_exact(case):
+    """Integer-valued operands with NaN in every padding column: the product must equal the
+    oracle's exact result rounded to bf16, bit for bit, whatever kernel the shape lands on."""
+    entry, M, N, K, lda, ldb, ldc = RANDOM_CASES[case]
+    A = matrix("int", M, K, seed=1000 + case, ld=lda)
+    B = matrix("int", K, N, seed=2000 + case, ld=ldb)
+    C = run(entry, A, B, M, N, K, ldc=ldc)
+    kernel = g.gemm_last_plan()["kernel"]
+    check_exact(C, A, B, M, N, K, f"{entry} {M}x{N}x{K} ld {lda},{ldb},{ldc} ({kernel})")
