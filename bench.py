@@ -485,6 +485,46 @@ def main():
                             "power_w_median": round(float(np.median(watts)), 1) if watts else None}
         del Al, Bl, Cl
 
+    # ---------------- the matrix cores on random operands ----------------
+    # The register-only loop above toggles few operand bits, so it measures the matrix cores at
+    # the clock limit. The products multiply random data, and under the board's power limit the
+    # clock then drops: this loop (the large-tile kernel's MFMA shape and register layout, random
+    # bf16 operands, no memory traffic) measures the ceiling for that data.
+    if not args.no_peaks:
+        log("MFMA rate on random operands")
+        ops = torch.randn(3072 * 8, device="cuda").to(torch.bfloat16)
+        dblocks = torch.cuda.get_device_properties(0).multi_processor_count
+        dsink = torch.zeros(dblocks * 512, dtype=torch.float32, device="cuda")
+        dcyc = torch.zeros(2 * dblocks, dtype=torch.int64, device="cuda")
+        dflop_per_iter = dblocks * 8 * 32 * 16384
+
+        def data_run(iters):
+            e0, e1 = events(2)
+            e0.record(stream)
+            g.gemm_peak_mfma_data_launch(P(ops), iters, dblocks, P(dsink), P(dcyc), sh)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            c = dcyc.view(-1, 2).double()
+            return dflop_per_iter * iters / (ms * 1e-3) / 1e12, ms, float((c[:, 0] / c[:, 1]).mean()) * 0.1
+
+        t_end = time.time() + RAMP_MS / 1e3
+        while time.time() < t_end:
+            data_run(20000)
+        sampler = PowerSampler()
+        with sampler:
+            rnd_tf, rnd_ms, rnd_clk = data_run(2_000_000)
+        watts = [x[1] for x in sampler.samples[1:] if x[1] is not None]
+        peaks["mfma_bf16_fp32_tflops_sustained_random_operands"] = round(rnd_tf, 1)
+        peaks["mfma_random_operands_ms"] = round(rnd_ms, 1)
+        peaks["shader_clock_ghz_random_operands"] = round(rnd_clk, 3)
+        peaks["mfma_random_operands_power_w_median"] = round(float(np.median(watts)), 1) if watts else None
+        headline["frac_of_random_operand_mfma_peak"] = round(achieved / rnd_tf, 4)
+        for rec in compute.values():
+            if "roofline" in rec:
+                rec["frac_of_random_operand_mfma_peak"] = round(rec["tflops_median"] / rnd_tf, 4)
+        del ops, dsink, dcyc
+
     # ---------------- decode workloads (HBM bound) ----------------
     if not args.no_decode:
         dec = {}

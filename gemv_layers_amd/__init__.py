@@ -33,7 +33,7 @@ EXPORTS = (
     "gemm_init", "gemm_bf16", "gemm_bf16_noalloc", "gemm_bf16_skinny", "gemm_bf16_tiled", "gemm_bf16_swiglu",
     "gemm_plan_describe",
     "gemm_wave_efficiency", "gemm_last_plan", "gemm_status_string", "gemm_finalize",
-    "gemm_peak_mfma_launch", "gemm_peak_copy_launch", "gemm_peak_read_launch",
+    "gemm_peak_mfma_launch", "gemm_peak_mfma_data_launch", "gemm_peak_copy_launch", "gemm_peak_read_launch",
     "gemm_peak_clock_launch", "gemm_peak_xcc_launch",
     "gemm_peak_empty_launch", "gemm_fill_launch",
     "gemm_mx_packed_sizes", "gemm_mx_pack_weight", "gemm_mx_quantize_act", "gemm_mx_decode",
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_finalize.restype = i32
     L.gemm_peak_mfma_launch.argtypes = [i64, i32, p, p, p]
     L.gemm_peak_mfma_launch.restype = i32
+    L.gemm_peak_mfma_data_launch.argtypes = [p, i64, i32, p, p, p]
+    L.gemm_peak_mfma_data_launch.restype = i32
     L.gemm_peak_copy_launch.argtypes = [p, p, i64, p]
     L.gemm_peak_copy_launch.restype = i32
     L.gemm_peak_read_launch.argtypes = [p, i64, p, p]
@@ -224,6 +226,11 @@ def gemm_peak_read_launch(src, nbytes, sink, stream=None) -> None:
 
 def gemm_peak_clock_launch(iters, blocks, out, stream=None) -> None:
     _check("gemm_peak_clock_launch", lib().gemm_peak_clock_launch(iters, blocks, out, stream))
+
+
+def gemm_peak_mfma_data_launch(ops, iters, blocks, sink, cycles, stream=None) -> None:
+    _check("gemm_peak_mfma_data_launch",
+           lib().gemm_peak_mfma_data_launch(ops, iters, blocks, sink, cycles, stream))
 
 
 def gemm_peak_xcc_launch(blocks, out, stream=None) -> None:

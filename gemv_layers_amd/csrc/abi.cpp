@@ -660,6 +660,16 @@ int gemm_peak_mfma_launch(int64_t iters, int blocks, float* sink, uint64_t* cycl
                : GEMM_ERR_HIP;
 }
 
+int gemm_peak_mfma_data_launch(const void* ops, int64_t iters, int blocks, float* sink, uint64_t* cycles,
+                               gemm_stream_t stream) {
+    if (iters < 0 || blocks <= 0 || !ops || !sink || !cycles || (reinterpret_cast<uintptr_t>(ops) & 15))
+        return GEMM_ERR_INVALID_ARG;
+    return glk::launch_peak_mfma_data(ops, iters, blocks, sink, cycles, reinterpret_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? GEMM_OK
+               : GEMM_ERR_HIP;
+}
+
 int gemm_peak_copy_launch(const void* src, void* dst, int64_t bytes, gemm_stream_t stream) {
     if (bytes < 0 || (bytes & 15) || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15))
         return GEMM_ERR_INVALID_ARG;

@@ -43,6 +43,56 @@ __global__ void __launch_bounds__(256) peak_mfma_kernel(int64_t iters, float* si
     }
 }
 
+// The matrix cores' rate on operands read from memory: v_mfma_f32_16x16x32_bf16 in the register
+// layout of the large-tile kernel's wave tile (128 float accumulators per lane in 4 x 8 16 x 16
+// blocks, 8 waves per workgroup, 2 per SIMD), 32 instructions per iteration on 8 A and 4 B
+// operand registers loaded once from `ops`. Under the board's power limit the clock depends on
+// how many operand bits toggle: random operands give the ceiling for products of random data,
+// where the register-only loop above, with near-constant operands, gives the ceiling at the
+// clock limit. Each instruction is 2 * 16 * 16 * 32 = 16384 flops.
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+peak_mfma_data_kernel(const u32x4* __restrict__ ops, int64_t iters, float* sink, uint64_t* cycles) {
+    const int t = threadIdx.x;
+    bf16x8 a[8], b[4];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = __builtin_bit_cast(bf16x8, ops[(q * 512 + t) & 2047]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[q] = __builtin_bit_cast(bf16x8, ops[2048 + ((q * 512 + t) & 1023)]);
+    wait_all_memory();  // operands in registers before the timed loop
+    __syncthreads();
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(b[i], a[j], acc[i][j]);
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += acc[i][j][0] + acc[i][j][1] + acc[i][j][2] + acc[i][j][3];
+    sink[(size_t)blockIdx.x * 512 + t] = s;
+    if (t == 0) {
+        cycles[2 * (size_t)blockIdx.x] = t1 - t0;
+        cycles[2 * (size_t)blockIdx.x + 1] = r1 - r0;
+    }
+}
+
+hipError_t launch_peak_mfma_data(const void* ops, int64_t iters, int blocks, float* sink, uint64_t* cycles,
+                                 hipStream_t s) {
+    peak_mfma_data_kernel<<<blocks, 512, 0, s>>>(static_cast<const u32x4*>(ops), iters, sink, cycles);
+    return hipGetLastError();
+}
+
 __global__ void __launch_bounds__(256) peak_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                         int64_t n16) {
     const int64_t stride = (int64_t)gridDim.x * 256 * 4;

@@ -320,6 +320,21 @@ int gemm_finalize(void);
 int gemm_peak_mfma_launch(int64_t iters, int blocks, float *sink, uint64_t *cycles,
                           gemm_stream_t stream);
 
+/*
+ * gemm_peak_mfma_data_launch: the matrix-core rate on operands from memory. `blocks` workgroups
+ * of 512 threads (8 waves, 2 per SIMD) each run `iters` iterations of 32 v_mfma_f32_16x16x32_bf16
+ * per wave into 128 float accumulators per lane (the large-tile kernel's wave-tile layout), on
+ * 8 A and 4 B operand registers per lane loaded once from `ops` (device, 16-byte aligned, at
+ * least 3072 * 16 = 49152 bytes: lane t of the workgroup reads 16-byte words (q * 512 + t) % 2048
+ * for A register q and 2048 + (q * 512 + t) % 1024 for B register q). flops = blocks * 8 waves *
+ * iters * 32 * 16384. `sink` (device, >= blocks * 512 floats) and `cycles` (device, >= 2 *
+ * blocks uint64) as for gemm_peak_mfma_launch. Random operands measure the ceiling the board's
+ * power limit leaves for products of random data (the register-only loop's near-constant
+ * operands toggle few bits and measure the clock-limited ceiling).
+ */
+int gemm_peak_mfma_data_launch(const void *ops, int64_t iters, int blocks, float *sink,
+                               uint64_t *cycles, gemm_stream_t stream);
+
 /* gemm_peak_copy_launch: dst[0 .. bytes) = src[0 .. bytes) with 16-byte loads and stores;
  * bytes must be a multiple of 16 and both pointers 16-byte aligned. HBM traffic = 2 * bytes. */
 int gemm_peak_copy_launch(const void *src, void *dst, int64_t bytes, gemm_stream_t stream);

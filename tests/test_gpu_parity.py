@@ -488,6 +488,25 @@ def test_measurement_kernels_run_and_copy_is_exact():
     assert 0.3 < float(ghz.median()) < 3.0
 
 
+def test_mfma_data_peak_closed_form():
+    """The operand-from-memory MFMA loop: A words all 1.0 and B words all 2.0 make every
+    16 x 16 x 32 product add 64 to each accumulator, so after `iters` iterations each lane's sum
+    of its 128 accumulators is 128 * 64 * iters exactly (a wrong operand word or a dropped
+    instruction changes it)."""
+    words = torch.empty(3072 * 8, dtype=torch.bfloat16, device="cuda")
+    words[: 2048 * 8] = 1.0
+    words[2048 * 8:] = 2.0
+    blocks, iters = 256, 100
+    sink = torch.zeros(blocks * 512, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    g.gemm_peak_mfma_data_launch(ctypes.c_void_p(words.data_ptr()), iters, blocks,
+                                 ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(cyc.data_ptr()),
+                                 g.current_stream_handle())
+    torch.cuda.synchronize()
+    assert torch.all(sink == 128 * 64 * iters)
+    assert torch.all(cyc > 0)
+
+
 # ---- concurrent streams and XCD placement ------------------------------------------------------
 
 def test_split_layouts_on_two_streams_at_once():
