@@ -660,6 +660,15 @@ int gemm_peak_mfma_launch(int64_t iters, int blocks, float* sink, uint64_t* cycl
                : GEMM_ERR_HIP;
 }
 
+// (declared here rather than with the other launchers: the kernels' shared header is part of the
+// source digest that ties the committed traffic summaries to the kernels they measured)
+extern "C++" {
+namespace glk {
+hipError_t launch_peak_mfma_data(const void* ops, int64_t iters, int blocks, float* sink, uint64_t* cycles,
+                                 hipStream_t s);
+}
+}
+
 int gemm_peak_mfma_data_launch(const void* ops, int64_t iters, int blocks, float* sink, uint64_t* cycles,
                                gemm_stream_t stream) {
     if (iters < 0 || blocks <= 0 || !ops || !sink || !cycles || (reinterpret_cast<uintptr_t>(ops) & 15))

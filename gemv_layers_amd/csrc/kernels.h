@@ -139,8 +139,6 @@ hipError_t launch_zero_c(uint16_t* C, int64_t M, int64_t N, int64_t ldc, hipStre
 hipError_t launch_fill(void* dst, int64_t bytes, uint32_t value, hipStream_t s);
 hipError_t launch_peak_mfma(int64_t iters, int blocks, float* sink, uint64_t* cycles,
                             hipStream_t s);
-hipError_t launch_peak_mfma_data(const void* ops, int64_t iters, int blocks, float* sink, uint64_t* cycles,
-                                 hipStream_t s);
 hipError_t launch_peak_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 hipError_t launch_peak_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_peak_empty(hipStream_t s);
