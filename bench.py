@@ -56,11 +56,12 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the tile kernel from the stored rocprofv3 FETCH_SIZE / WRITE_SIZE
-    passes (each scaled by the copy-kernel calibration), or None when there is no stored reading
-    for this workload or the kernel's sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"tile_gemm_{workload}_traffic.txt")
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` ("tile" or "skinny") on `workload` from the stored
+    rocprofv3 FETCH_SIZE / WRITE_SIZE passes (each scaled by the copy-kernel calibration), or
+    None when there is no stored reading for it or the kernel's sources changed since it was
+    taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_gemm_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -69,9 +70,10 @@ def measured_traffic(workload: str):
             if ":" in ln and not ln.startswith("#"):
                 k, v = ln.split(":", 1)
                 kv[k.strip()] = v.strip()
-    from gemv_layers_amd.profiling import TILE_SOURCES, source_digest
+    from gemv_layers_amd.profiling import SKINNY_SOURCES, TILE_SOURCES, source_digest
 
-    if kv.get("source_sha256") != source_digest(TILE_SOURCES) or "traffic_bytes_per_launch" not in kv:
+    sources = TILE_SOURCES if kernel == "tile" else SKINNY_SOURCES
+    if kv.get("source_sha256") != source_digest(sources) or "traffic_bytes_per_launch" not in kv:
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
 
@@ -649,7 +651,8 @@ def main():
                    "gbps_graph_replay": round(wd.bytes / (graph_us * 1e-6) / 1e9, 1),
                    "algorithmic_bytes": wd.bytes,
                    "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": MI355X_PEAK_HBM_GBPS,
-                                "unit": "GB/s", "frac": round(gbps / MI355X_PEAK_HBM_GBPS, 4)},
+                                "unit": "GB/s", "frac": round(gbps / MI355X_PEAK_HBM_GBPS, 4),
+                                "traffic": measured_traffic("skinny", name)},
                    "plan_splits": g.gemm_last_plan().get("splits")}
             if "hbm_copy_gbps" in peaks:
                 rec["frac_of_measured_copy"] = round(gbps / peaks["hbm_copy_gbps"], 4)
@@ -909,7 +912,7 @@ def main():
 
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(w.name)}
+                "traffic": measured_traffic("tile", w.name)}
     if w.name in compute:
         roofline["achieved_cache_flushed"] = compute[w.name]["tflops_cache_flushed"]
         roofline["frac_cache_flushed"] = round(compute[w.name]["tflops_cache_flushed"] / MI355X_PEAK_BF16_TFLOPS, 4)
