@@ -19,8 +19,9 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 // Workspace region, one per (device, stream): float32 partial slots for split tiles / K slices,
-// and their arrival counters. On 256 CUs no plan needs more than 4 Mi floats of partials (16 MiB:
-// 256 split pieces of a 128 x 128 tile, or two 16 x 64 x 128 skinny slots per workgroup).
+// and their arrival counters. On 256 CUs no plan needs more than 8 Mi floats of partials (32 MiB:
+// 512 split pieces of a 128 x 128 tile, two per CU; the skinny kernel's two 16 x 64 x 128 slots
+// per workgroup take 4 Mi).
 constexpr int64_t kWsFloats = int64_t(8) << 20;   // 32 MiB
 constexpr int64_t kWsCounters = int64_t(1) << 16;
 // The last 16 MiB of a region hold the MXFP8 activations that gemm_mx_decode_bf16 quantises
@@ -40,9 +41,9 @@ struct Region {
 
 // Workspace of gemm_bf16_noalloc, for callers that cannot allocate: a file-scope device array
 // (each GPU the library runs on holds its own copy until the process ends), arrival counters
-// first, then float32 partial slots. 4 Mi floats hold the largest split plan on 256 CUs.
+// first, then float32 partial slots. 8 Mi floats hold the largest split plan on 256 CUs.
 constexpr int64_t kScratchCounters = int64_t(1) << 14;   // 64 KiB
-constexpr int64_t kScratchFloats = int64_t(4) << 20;     // 16 MiB
+constexpr int64_t kScratchFloats = int64_t(8) << 20;     // 32 MiB
 static __device__ __align__(256) uint32_t scratch[kScratchCounters + kScratchFloats];
 
 struct DeviceState {

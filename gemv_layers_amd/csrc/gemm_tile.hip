@@ -105,8 +105,10 @@ __device__ __forceinline__ int a_swz(int c, int m) { return c ^ ((m >> 1) & 7); 
 __device__ __forceinline__ int b_swz(int u, int k) { return u ^ ((k & 3) | ((k >> 1) & 4)); }
 
 template <int BM, int BN, int WM, int WN, bool GLU>
+// (two waves per SIMD: at most 256 registers per lane, so two 128 x 128 workgroups fit on a CU
+// together, and one 256 x 256 workgroup's eight waves fit at all)
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
-                               amdgpu_waves_per_eu(1, 1)))
+                               amdgpu_waves_per_eu(2, 2)))
 tile_gemm_kernel(TileArgs p) {
     using T = TileTraits<BM, BN, WM, WN>;
     static_assert(!GLU || (T::TN % 2 == 0), "SwiGLU pairs gate and up tiles within a wave");

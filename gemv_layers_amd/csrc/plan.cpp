@@ -135,19 +135,22 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     // the tests see (measured interleaved, settled clocks: sq8192 807 against 828 us, mlp_up 300
     // against 309 us, mlp_down 271 against 278 us)
     set_tile(p, kTile256x256pp, M, N);
-    // A 128x128 tile takes about half as long as a 256x256 one (51 against 90 us at K = 4096 in a
-    // partial wave), but a second 128x128 workgroup on a CU does not overlap the first: a grid of
-    // more small tiles than CUs takes two of their waves (99 us for 272 to 336 tiles). So the
-    // small tiles serve only grids they cover in one wave (measured, settled clocks: 2048^3 as
-    // 256 small tiles 28 us against 50 us as 64 big ones; 1024 x 4352 x 4096 as 68 big tiles
-    // 90 us against 99 us as 272 small ones).
+    // Below one wave of 256x256 tiles, 128x128 tiles: one alone on a CU takes about 60% as long
+    // as a 256x256 one (46 against 77 us at K = 4096), and two share a CU (72 KB of LDS and at
+    // most 256 registers per lane each), taking about 1.35 times as long together as one alone.
+    // So up to two small tiles per CU beat one partial wave of big ones; beyond that the big
+    // tiles' lower bytes per flop win (measured, settled clocks: 2048^3 as 256 small tiles 26 us
+    // against 41 us as 64 big ones; at K = 4096, 272 to 344 small tiles 61-63 us against 76-77
+    // us as 68 to 86 big ones, 512 small tiles 74-76 us against 77 us as 128 big ones, 768
+    // small tiles 112 us against 86 us as 192 big ones).
+    const int64_t small_tiles = cdiv(M, tile_shape(kTile128x128w4).bm) * cdiv(N, tile_shape(kTile128x128w4).bn);
     if (p.tiles >= dev.cus) {
         p.reason = "256x256 tiles fill at least one wave";
-    } else if (cdiv(M, tile_shape(kTile128x128w4).bm) * cdiv(N, tile_shape(kTile128x128w4).bn) > dev.cus) {
-        p.reason = "128x128 tiles would need a second wave: 256x256 tiles";
+    } else if (small_tiles > 2 * (int64_t)dev.cus) {
+        p.reason = "128x128 tiles would need more than two per CU: 256x256 tiles";
     } else {
         set_tile(p, kTile128x128w4, M, N);
-        p.reason = "128x128 tiles in one wave";
+        p.reason = small_tiles > dev.cus ? "128x128 tiles, up to two per CU" : "128x128 tiles in one wave";
     }
     if (dev.force_tile_cfg >= 0 && dev.force_tile_cfg < kTileConfigCount) {
         set_tile(p, dev.force_tile_cfg, M, N);
@@ -158,21 +161,34 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     p.sched = kSchedDataParallel;
     p.splits = 1;
     p.kt_per_split = (int)kt_total;
-    // one workgroup per CU at a time: the 256-wide tile takes all of LDS, and a second 128x128
-    // workgroup on a CU does not overlap the first (measured)
-    p.slots = (int64_t)dev.cus;
-    // only the smaller tiles carry the split fixup
-    if (p.tiles < p.slots && kt_total > 1 && p.tile_cfg == kTile128x128w4) {
+    // workgroups resident at once: one per CU for the 256-wide tile (it takes all of LDS), two for
+    // the 128x128 one
+    p.slots = (int64_t)dev.cus * (p.tile_cfg == kTile128x128w4 ? 2 : 1);
+    // only the smaller tiles carry the split fixup, and only grids that leave CUs idle
+    if (p.tiles < dev.cus && kt_total > 1 && p.tile_cfg == kTile128x128w4) {
         // split K over the idle CUs; pieces are summed in K order by the last arriver, which
         // reads every other piece's float32 tile (BM*BN*4 bytes), one memory round trip per piece
-        // (about 1.2 us), against about 0.4 us per k-step of a lone 128x128 workgroup. So the
-        // pieces number about sqrt(kt / 3), and at most one workgroup per CU: two co-resident
-        // pieces of different tiles ran slower than one unsplit tile (measured, settled clocks:
-        // 2048^3 unsplit 30 us against 42 us in 2 pieces per tile; 1024 x 1024 x 8192 in 4 pieces
-        // 35 us against 50 us in 8; 128 x 128 x 65536 in 32 pieces 48 us against 160 us in 256).
-        int64_t root = 1;
-        while ((root + 1) * (root + 1) * 3 <= kt_total) ++root;
-        int64_t s = std::min<int64_t>(root, std::max<int64_t>(1, dev.cus / p.tiles));
+        // (about 1.2 us), against about 0.4 us per k-step of a lone 128x128 workgroup. So with
+        // at most one piece per CU the pieces number about sqrt(kt / 3) (measured, settled
+        // clocks: 1024 x 1024 x 8192 in 4 pieces 32 us against 36 us in 8, two per CU; 1024 x
+        // 2048 x 4096 in 2 pieces 30 us against 32 us in 4). When more than half the CUs hold a
+        // tile, one piece per CU cannot split at all, and two per CU pay: co-resident pieces
+        // run together at about 1.35 times a lone one's time, but each costs about 3.5-4 us of
+        // fixup, so about sqrt(kt / 8) pieces, and none below 96 k-steps (K = 4096: 144 tiles in
+        // 3 pieces 33 us against 46 us, 169 in 3 35.5 against 46, 240 in 2 42 against 46.6;
+        // 144 tiles at K = 1024 in 3 pieces 19.8 against 15.7 us, 196 at K = 2048 in 2 26.4
+        // against 26.1).
+        const int64_t per_cu = dev.cus / p.tiles;
+        int64_t s = 1;
+        if (per_cu >= 2) {
+            int64_t root = 1;
+            while ((root + 1) * (root + 1) * 3 <= kt_total) ++root;
+            s = std::min<int64_t>(root, per_cu);
+        } else if (kt_total >= 96) {
+            int64_t root = 1;
+            while ((root + 1) * (root + 1) * 8 <= kt_total) ++root;
+            s = std::min<int64_t>(root, 2 * dev.cus / p.tiles);
+        }
         s = std::max<int64_t>(s, 1);
         const int64_t slot_floats = (int64_t)p.bm * p.bn;
         while (s > 1 && p.tiles * s * slot_floats > dev.ws_floats) --s;

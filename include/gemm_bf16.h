@@ -85,12 +85,12 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
  * gemm_bf16_noalloc: gemm_bf16 for callers that cannot allocate device memory (code under graph
  * capture that must not make a workspace, tight serving loops, harnesses that forbid hipMalloc).
  * Same arguments, plan, kernels and bits as gemm_bf16, but the split partials and arrival counters
- * live in a fixed library array of 16 MiB of float32 slots plus 16384 counters per GPU, held from
+ * live in a fixed library array of 32 MiB of float32 slots plus 16384 counters per GPU, held from
  * the library's load until the process ends, instead of the stream's workspace region; the call
  * never allocates or frees. gemm_init must have run on the device. A plan whose partials or
  * counters exceed that array returns GEMM_ERR_UNSUPPORTED (on 256 CUs none does: the largest
- * split plan needs exactly 4 Mi floats, and the fast kernels take at most 2^20 columns, 8192
- * strips). Every call on one GPU shares the one array:
+ * split plan needs exactly 8 Mi floats, 512 pieces of a 128 x 128 tile, and the fast kernels
+ * take at most 2^20 columns, 8192 strips). Every call on one GPU shares the one array:
  * calls that overlap in time on that GPU, on any streams, race and must be serialised by the
  * caller. Counters return to zero at the end of every call.
  */

@@ -79,8 +79,10 @@ def check_exact(C, A, B, M, N, K, what=""):
 
 TILE_SHAPES = [(256, 256, 64), (512, 512, 512), (300, 520, 328), (1000, 1000, 1000),
                (65, 264, 72), (1, 8, 8), (257, 264, 4104), (513, 1032, 136),
-               # 256 x 256 tiles in a partial wave (80 and 108 tiles), ragged in M, N and K
-               (1000, 5000, 328), (777, 6704, 200)]
+               # 128 x 128 tiles up to two per CU (320 and 371 tiles), ragged in M, N and K
+               (1000, 5000, 328), (777, 6704, 200),
+               # 256 x 256 tiles in a partial wave (144 and 172 tiles), ragged in M, N and K
+               (1000, 9000, 328), (777, 11000, 200)]
 
 
 @pytest.mark.parametrize("M,N,K", TILE_SHAPES)
@@ -91,8 +93,9 @@ def test_tile_kernel_float_and_exact(M, N, K):
     Ai = matrix("int", M, K, seed=3000 + M)
     Bi = matrix("int", K, N, seed=4000 + N)
     check_exact(run("tiled", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"tiled int {M}x{N}x{K}")
-    if (-(-M // 128)) * (-(-N // 128)) > 256:  # 128 x 128 tiles would need a second wave
-        assert g.gemm_last_plan()["bm"] == 256
+    big, small = (-(-M // 256)) * (-(-N // 256)), (-(-M // 128)) * (-(-N // 128))
+    # 256 x 256 tiles from one full wave of them, or when 128 x 128 ones would need three per CU
+    assert g.gemm_last_plan()["bm"] == (256 if big >= 256 or small > 512 else 128)
 
 
 SKINNY_SHAPES = [(m, n, k) for m in (1, 2, 3, 16, 17, 33, 64)
@@ -570,7 +573,7 @@ def test_tile_schedules_give_the_same_bits():
     import os
     import subprocess
     import sys
-    M, N, K = 777, 6704, 1000
+    M, N, K = 777, 11000, 1000
     A = matrix("normal", M, K, seed=31000)
     B = matrix("normal", K, N, seed=32000, sigma=0.5)
     mine = run("tiled", A, B, M, N, K)

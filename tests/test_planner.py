@@ -71,22 +71,35 @@ def test_small_square_splits_k():
 @pytest.mark.parametrize("M,N,K", [(512, 512, 512), (1000, 1000, 1000), (257, 264, 4104),
                                    (300, 520, 328), (128, 128, 96), (200, 2000, 20000),
                                    (2048, 2048, 2048), (1024, 1024, 8192), (128, 128, 65536),
-                                   (2048, 1024, 4096)])
+                                   (2048, 1024, 4096), (1536, 1536, 4096), (1664, 1664, 4096),
+                                   (1536, 1536, 96), (2048, 1920, 4096), (1536, 1536, 1024),
+                                   (1792, 1792, 2048), (1536, 1536, 3072)])
 def test_split_count_follows_the_measured_rule(M, N, K):
     # each piece costs the last arriver one memory round trip, about three k-steps of a lone
-    # workgroup, so K is cut into about sqrt(kt / 3) pieces, and into no more pieces than leave
-    # one workgroup per CU; no piece is empty
+    # workgroup, so with one workgroup per CU K is cut into about sqrt(kt / 3) pieces; when only
+    # one piece per tile would fit that way, up to two per CU, about sqrt(kt / 8) pieces and only
+    # from 96 k-steps; grids with a tile per CU stay whole; no piece is empty
     p = g.gemm_plan_describe(M, N, K, 256)
     kt = -(-K // p["bk"])
-    root = 1
-    while 3 * (root + 1) ** 2 <= kt:
-        root += 1
-    want = max(1, min(root, 256 // p["tiles"])) if p["bm"] == 128 else 1
+
+    def root(c):
+        r = 1
+        while c * (r + 1) ** 2 <= kt:
+            r += 1
+        return r
+
+    want = 1
+    if p["bm"] == 128 and p["tiles"] < 256:
+        per_cu = 256 // p["tiles"]
+        if per_cu >= 2:
+            want = min(root(3), per_cu)
+        elif kt >= 96:
+            want = min(root(8), 512 // p["tiles"])
     if want > 1:
         per = -(-kt // want)
         assert p["schedule"] == "split-k" and p["kt_per_split"] == per and p["splits"] == -(-kt // per)
         assert (p["splits"] - 1) * p["kt_per_split"] < kt <= p["splits"] * p["kt_per_split"]
-        assert p["grid"] == p["tiles"] * p["splits"] <= 256
+        assert p["grid"] == p["tiles"] * p["splits"] <= 512
     else:
         assert p["splits"] == 1 and p["schedule"] == "data-parallel"
 
@@ -195,16 +208,20 @@ def test_mx_plan_rejects_other_shapes():
             g.gemm_plan_describe(M, N, K, mx=True)
 
 
-@pytest.mark.parametrize("M,N,K,bm", [(1024, 11008, 4096, 256), (512, 11008, 4096, 256), (3072, 4096, 4096, 256),
+@pytest.mark.parametrize("M,N,K,bm", [(1024, 11008, 4096, 256), (512, 11008, 4096, 128), (3072, 4096, 4096, 256),
                                       (2048, 2048, 2048, 128), (1024, 4096, 11008, 128),
-                                      (1024, 4352, 4096, 256), (1024, 4096, 4096, 128),
-                                      (1000, 4104, 512, 256), (1000, 4096, 512, 128)])
-def test_small_tiles_only_in_one_wave(M, N, K, bm):
-    # a second 128 x 128 workgroup on a CU does not overlap the first, so 128 x 128 tiles serve
-    # only grids they cover in one wave; otherwise 256 x 256 tiles, in a partial wave if need be
+                                      (1024, 4352, 4096, 128), (1024, 4096, 4096, 128),
+                                      (1000, 4104, 512, 128), (1000, 4096, 512, 128),
+                                      (2048, 4096, 4096, 128), (2048, 4224, 4096, 256),
+                                      (4096, 4096, 4096, 256)])
+def test_small_tiles_up_to_two_per_cu(M, N, K, bm):
+    # below one wave of 256 x 256 tiles, 128 x 128 tiles as long as at most two share a CU (two
+    # fit in a CU's LDS and registers and run together); otherwise 256 x 256 tiles
     p = g.gemm_plan_describe(M, N, K, 256)
     assert p["kernel"] == "tile" and p["bm"] == bm, p
+    big = -(-M // 256) * -(-N // 256)
     small = -(-M // 128) * -(-N // 128)
-    assert (small <= 256) == (bm == 128)
-    if bm == 256:
+    assert (big < 256 and small <= 512) == (bm == 128)
+    assert p["slots"] == (512 if bm == 128 else 256)
+    if bm == 256 or small >= 256:
         assert p["splits"] == 1 and p["schedule"] == "data-parallel"
