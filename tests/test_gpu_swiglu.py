@@ -163,3 +163,35 @@ def test_llama7b_gate_up_prefill_sampled_rows():
         h, slack = osw.swiglu_rows(A, B, r, 1, N, K)
         res = osw.check(C[r: r + 1], h, slack)
         assert res.ok, f"row {r}: {res.summary()}"
+
+
+# ---- seeded random shapes across every dispatch regime ---------------------------------------
+
+def _random_glu_cases(n, seed=20251203):
+    """(M, N, K) from a fixed seed: M in the skinny, small-tile and large-tile ranges; N and K
+    multiples of 8 (the fast kernels) or arbitrary (the general kernel); at most 1e9 multiply-adds
+    over the gate and up halves together."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        regime = rng.choice(3, p=[0.4, 0.3, 0.3])
+        M = int(rng.integers(1, 65) if regime == 0 else rng.integers(65, 400) if regime == 1
+                else rng.integers(400, 1100))
+        N, K = int(rng.integers(1, 2000)), int(rng.integers(1, 1600))
+        if rng.random() < 0.75:
+            N, K = max(8, N - N % 8), max(8, K - K % 8)
+        if 2 * M * N * K <= 1e9:
+            cases.append((M, N, K))
+    return cases
+
+
+RANDOM_GLU = _random_glu_cases(24)
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_GLU)))
+def test_random_shapes_swiglu(case):
+    M, N, K = RANDOM_GLU[case]
+    A = matrix("normal", M, K, seed=7700 + case)
+    B = matrix("normal", K, 2 * N, seed=7800 + case, sigma=0.02)
+    C, plan = run(A, B, M, N, K)
+    check(C, A, B, M, N, K, f"swiglu {M}x{N}x{K} ({plan['kernel']})")
