@@ -225,3 +225,23 @@ def test_small_tiles_up_to_two_per_cu(M, N, K, bm):
     assert p["slots"] == (512 if bm == 128 else 256)
     if bm == 256 or small >= 256:
         assert p["splits"] == 1 and p["schedule"] == "data-parallel"
+
+
+@pytest.mark.parametrize("cus", [80, 228, 256, 304])
+@pytest.mark.parametrize("M,N,K", [(1024, 4352, 4096), (2048, 2048, 4096), (1536, 1536, 4096),
+                                   (1024, 11008, 4096), (4096, 4096, 4096), (512, 512, 8192)])
+def test_tile_rules_follow_the_cu_count(cus, M, N, K):
+    # the tile choice and the K split scale with the queried CU count: 256 x 256 tiles from one
+    # full wave of them, else 128 x 128 tiles while at most two share a CU; a K split only for
+    # fewer small tiles than CUs, and then at most two pieces per CU
+    p = g.gemm_plan_describe(M, N, K, cus)
+    big = -(-M // 256) * -(-N // 256)
+    small = -(-M // 128) * -(-N // 128)
+    want_bm = 256 if (big >= cus or small > 2 * cus) else 128
+    assert p["bm"] == want_bm, p
+    assert p["slots"] == (2 * cus if want_bm == 128 else cus)
+    if p["schedule"] == "split-k":
+        assert want_bm == 128 and p["tiles"] < cus
+        assert p["grid"] <= 2 * cus
+        if cus // p["tiles"] >= 2:
+            assert p["grid"] <= cus
