@@ -164,8 +164,8 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     // workgroups resident at once: one per CU for the 256-wide tile (it takes all of LDS), two for
     // the 128x128 one
     p.slots = (int64_t)dev.cus * (p.tile_cfg == kTile128x128w4 ? 2 : 1);
-    // only the smaller tiles carry the split fixup, and only grids that leave CUs idle
-    if (p.tiles < dev.cus && kt_total > 1 && p.tile_cfg == kTile128x128w4) {
+    // only the smaller tiles carry the split fixup, and only grids of at most one tile per CU
+    if (p.tiles <= dev.cus && kt_total > 1 && p.tile_cfg == kTile128x128w4) {
         // split K over the idle CUs; pieces are summed in K order by the last arriver, which
         // reads every other piece's float32 tile (BM*BN*4 bytes), one memory round trip per piece
         // (about 1.2 us), against about 0.4 us per k-step of a lone 128x128 workgroup. So with
@@ -175,9 +175,10 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
         // tile, one piece per CU cannot split at all, and two per CU pay: co-resident pieces
         // run together at about 1.35 times a lone one's time, but each costs about 3.5-4 us of
         // fixup, so about sqrt(kt / 8) pieces, and none below 96 k-steps (K = 4096: 144 tiles in
-        // 3 pieces 33 us against 46 us, 169 in 3 35.5 against 46, 240 in 2 42 against 46.6;
-        // 144 tiles at K = 1024 in 3 pieces 19.8 against 15.7 us, 196 at K = 2048 in 2 26.4
-        // against 26.1).
+        // 3 pieces 33 us against 46 us, 169 in 3 35.5 against 46, 240 in 2 42 against 46.6, 256
+        // (one per CU) in 2 42.4 against 46.2; 256 tiles at K = 11008 in 2 94.9 against 116.2,
+        // at K = 3072 35.2 against 36.1, at K = 2048 28.0 against 25.9; 144 tiles at K = 1024 in
+        // 3 pieces 19.8 against 15.7 us, 196 at K = 2048 in 2 26.4 against 26.1).
         const int64_t per_cu = dev.cus / p.tiles;
         int64_t s = 1;
         if (per_cu >= 2) {

@@ -82,7 +82,9 @@ TILE_SHAPES = [(256, 256, 64), (512, 512, 512), (300, 520, 328), (1000, 1000, 10
                # 128 x 128 tiles up to two per CU (320 and 371 tiles), ragged in M, N and K
                (1000, 5000, 328), (777, 6704, 200),
                # 256 x 256 tiles in a partial wave (144 and 172 tiles), ragged in M, N and K
-               (1000, 9000, 328), (777, 11000, 200)]
+               (1000, 9000, 328), (777, 11000, 200),
+               # exactly one 128 x 128 tile per CU (256) and 97 k-steps: K split in two, ragged
+               (1000, 4000, 3080)]
 
 
 @pytest.mark.parametrize("M,N,K", TILE_SHAPES)
@@ -95,7 +97,10 @@ def test_tile_kernel_float_and_exact(M, N, K):
     check_exact(run("tiled", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"tiled int {M}x{N}x{K}")
     big, small = (-(-M // 256)) * (-(-N // 256)), (-(-M // 128)) * (-(-N // 128))
     # 256 x 256 tiles from one full wave of them, or when 128 x 128 ones would need three per CU
-    assert g.gemm_last_plan()["bm"] == (256 if big >= 256 or small > 512 else 128)
+    plan = g.gemm_last_plan()
+    assert plan["bm"] == (256 if big >= 256 or small > 512 else 128)
+    if (M, N, K) == (1000, 4000, 3080):
+        assert plan["splits"] == 2 and plan["grid"] == 512
 
 
 SKINNY_SHAPES = [(m, n, k) for m in (1, 2, 3, 16, 17, 33, 64)

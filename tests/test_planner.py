@@ -73,12 +73,13 @@ def test_small_square_splits_k():
                                    (2048, 2048, 2048), (1024, 1024, 8192), (128, 128, 65536),
                                    (2048, 1024, 4096), (1536, 1536, 4096), (1664, 1664, 4096),
                                    (1536, 1536, 96), (2048, 1920, 4096), (1536, 1536, 1024),
-                                   (1792, 1792, 2048), (1536, 1536, 3072)])
+                                   (1792, 1792, 2048), (1536, 1536, 3072), (1024, 4096, 4096),
+                                   (1024, 4096, 11008), (2048, 2048, 8192), (1024, 4096, 2048)])
 def test_split_count_follows_the_measured_rule(M, N, K):
     # each piece costs the last arriver one memory round trip, about three k-steps of a lone
     # workgroup, so with one workgroup per CU K is cut into about sqrt(kt / 3) pieces; when only
     # one piece per tile would fit that way, up to two per CU, about sqrt(kt / 8) pieces and only
-    # from 96 k-steps; grids with a tile per CU stay whole; no piece is empty
+    # from 96 k-steps; grids with more tiles than CUs stay whole; no piece is empty
     p = g.gemm_plan_describe(M, N, K, 256)
     kt = -(-K // p["bk"])
 
@@ -89,7 +90,7 @@ def test_split_count_follows_the_measured_rule(M, N, K):
         return r
 
     want = 1
-    if p["bm"] == 128 and p["tiles"] < 256:
+    if p["bm"] == 128 and p["tiles"] <= 256:
         per_cu = 256 // p["tiles"]
         if per_cu >= 2:
             want = min(root(3), per_cu)
@@ -223,7 +224,7 @@ def test_small_tiles_up_to_two_per_cu(M, N, K, bm):
     small = -(-M // 128) * -(-N // 128)
     assert (big < 256 and small <= 512) == (bm == 128)
     assert p["slots"] == (512 if bm == 128 else 256)
-    if bm == 256 or small >= 256:
+    if bm == 256 or small > 256:
         assert p["splits"] == 1 and p["schedule"] == "data-parallel"
 
 
@@ -232,8 +233,8 @@ def test_small_tiles_up_to_two_per_cu(M, N, K, bm):
                                    (1024, 11008, 4096), (4096, 4096, 4096), (512, 512, 8192)])
 def test_tile_rules_follow_the_cu_count(cus, M, N, K):
     # the tile choice and the K split scale with the queried CU count: 256 x 256 tiles from one
-    # full wave of them, else 128 x 128 tiles while at most two share a CU; a K split only for
-    # fewer small tiles than CUs, and then at most two pieces per CU
+    # full wave of them, else 128 x 128 tiles while at most two share a CU; a K split only while
+    # the small tiles are no more than the CUs, and then at most two pieces per CU
     p = g.gemm_plan_describe(M, N, K, cus)
     big = -(-M // 256) * -(-N // 256)
     small = -(-M // 128) * -(-N // 128)
@@ -241,7 +242,7 @@ def test_tile_rules_follow_the_cu_count(cus, M, N, K):
     assert p["bm"] == want_bm, p
     assert p["slots"] == (2 * cus if want_bm == 128 else cus)
     if p["schedule"] == "split-k":
-        assert want_bm == 128 and p["tiles"] < cus
+        assert want_bm == 128 and p["tiles"] <= cus
         assert p["grid"] <= 2 * cus
         if cus // p["tiles"] >= 2:
             assert p["grid"] <= cus
