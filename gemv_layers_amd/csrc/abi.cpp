@@ -131,6 +131,33 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     return GEMM_OK;
 }
 
+// one launch of the large-tile kernel family for plan `p` over an M x N output (N outputs, 2N weight
+// columns in the SwiGLU form)
+hipError_t launch_tile_plan(const glk::Plan& p, int64_t M, int64_t N, int64_t K, const uint16_t* a16,
+                            int64_t lda, const uint16_t* b16, int64_t ldb, uint16_t* c16, int64_t ldc,
+                            bool glu, const Region* rg, hipStream_t stream) {
+    glk::TileArgs t;
+    t.A = a16;
+    t.B = b16;
+    t.C = c16;
+    t.M = (int)M;
+    t.N = (int)N;
+    t.K = (int)K;
+    t.lda = (int)lda;
+    t.ldb = (int)ldb;
+    t.ldc = (int)ldc;
+    t.tiles_m = (int)p.tiles_m;
+    t.tiles_n = (int)p.tiles_n;
+    t.group_m = p.group_m;
+    t.nxcd = p.nxcd;
+    t.sched = p.sched;
+    t.splits = p.splits;
+    t.kt_per_split = p.kt_per_split;
+    t.ws = rg->ws;
+    t.counters = rg->counters;
+    return glk::launch_tile_gemm(p.tile_cfg, t, (int)p.grid, glu, stream);
+}
+
 // force: 0 dispatch on M, 1 skinny, 2 large-tile family; glu: the SwiGLU form; noalloc: split
 // partials and counters in the device's scratch array instead of the stream's region
 int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -180,26 +207,20 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void*
             e = glk::launch_generic_gemm(a16, b16, c16, M, N, K, lda, ldb, ldc, glu, stream);
             break;
         case glk::kKernTile: {
-            glk::TileArgs t;
-            t.A = a16;
-            t.B = b16;
-            t.C = c16;
-            t.M = (int)M;
-            t.N = (int)N;
-            t.K = (int)K;
-            t.lda = (int)lda;
-            t.ldb = (int)ldb;
-            t.ldc = (int)ldc;
-            t.tiles_m = (int)p.tiles_m;
-            t.tiles_n = (int)p.tiles_n;
-            t.group_m = p.group_m;
-            t.nxcd = p.nxcd;
-            t.sched = p.sched;
-            t.splits = p.splits;
-            t.kt_per_split = p.kt_per_split;
-            t.ws = rg->ws;
-            t.counters = rg->counters;
-            e = glk::launch_tile_gemm(p.tile_cfg, t, (int)p.grid, glu, stream);
+            // a cut plan covers the first cut_at columns (axis 1) or rows (axis 2); the strip left
+            // over runs next on the same stream with its own plan (only it may use the workspace)
+            const int64_t Mm = p.cut_axis == 2 ? p.cut_at : M;
+            const int64_t Nm = p.cut_axis == 1 ? p.cut_at : N;
+            e = launch_tile_plan(p, Mm, Nm, K, a16, lda, b16, ldb, c16, ldc, glu, rg, stream);
+            if (e == hipSuccess && p.cut_axis != 0) {
+                const glk::Plan& r = p.rest[0];
+                if (p.cut_axis == 1)
+                    e = launch_tile_plan(r, M, N - p.cut_at, K, a16, lda, b16 + p.cut_at, ldb, c16 + p.cut_at,
+                                         ldc, glu, rg, stream);
+                else
+                    e = launch_tile_plan(r, M - p.cut_at, N, K, a16 + p.cut_at * lda, lda, b16, ldb,
+                                         c16 + p.cut_at * ldc, ldc, glu, rg, stream);
+            }
             break;
         }
         case glk::kKernSkinny: {

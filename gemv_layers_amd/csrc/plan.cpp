@@ -210,6 +210,60 @@ static Plan plan_tile(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     return p;
 }
 
+// A last wave of 256 x 256 tiles that is at most half full takes most of a full wave's time for a
+// fraction of its work. Such a product is cut into the largest rectangle of whole tile rows or
+// columns that fits in the full waves, planned as before, and the strip left over, planned on its
+// own, which must come out as 128 x 128 tiles (at most two per CU, K split over idle CUs). Measured
+// against one launch, interleaved, settled clocks, us (last wave's tiles in brackets): 4096 x 4352
+// x 4096 (16) 121.7 against 170.5 (hipBLASLt 166.5), 4096 x 4608 x 4096 (32) 134.0 against 172.2,
+// 4352^2 x 4096 (33) 136.1 against 172.3, 4096 x 4864 x 4096 (48) 144.1 against 175.7, 4096 x
+// 5120 x 4096 (64) 147.1 against 173.3, 4608^3 (68) 181.0 against 194.3, 4096 x 5632 x 4096 (96)
+// 168.8 against 178.0, 4096 x 6144 x 4096 (128) 174.3 against 180.1, 6144^3 (64, after two full
+// waves) 379.5 against 391.1, 8192 x 8448 x 4096 (32, after four) 428.1 against 458.5; a fuller
+// last wave lost (4096 x 11008 x 4096, 176: 284.8 against 278.2; 5120^3, 144: 219.4 against
+// 217.2). The SwiGLU form is cut only across rows: its up half sits N weight columns after the
+// gate half, so a column strip would need both halves' offsets.
+static void cut_sparse_last_wave(Plan& p, int64_t M, int64_t W, int64_t K, const DeviceInfo& dev, bool glu) {
+    if (p.kernel != kKernTile || p.tile_cfg != kTile256x256pp || p.sched != kSchedDataParallel) return;
+    if (dev.force_tile_cfg >= 0) return;
+    const int64_t slots = p.slots;
+    const int64_t full = p.tiles / slots, last = p.tiles - full * slots;
+    if (full < 1 || last == 0 || 2 * last > slots) return;
+    const int64_t room = full * slots;
+    int axis = 0;
+    int64_t kept = 0, cut = 0;
+    if (!glu) {  // keep the first tn tile columns
+        const int64_t tn = room / p.tiles_m;
+        if (tn >= 1 && tn < p.tiles_n) {
+            axis = 1;
+            kept = tn * p.tiles_m;
+            cut = tn * p.bn;
+        }
+    }
+    {  // keep the first tm tile rows
+        const int64_t tm = room / p.tiles_n;
+        if (tm >= 1 && tm < p.tiles_m && tm * p.tiles_n > kept) {
+            axis = 2;
+            kept = tm * p.tiles_n;
+            cut = tm * p.bm;
+        }
+    }
+    if (axis == 0) return;
+    Plan rest = axis == 1 ? plan_tile(M, W - cut, K, dev) : plan_tile(M - cut, W, K, dev);
+    if (rest.tile_cfg != kTile128x128w4) return;
+    Plan q = axis == 1 ? plan_tile(M, cut, K, dev) : plan_tile(cut, W, K, dev);
+    q.glu = rest.glu = glu;
+    q.cut_axis = axis;
+    q.cut_at = cut;
+    q.ws_floats = std::max(q.ws_floats, rest.ws_floats);
+    q.counters = std::max(q.counters, rest.counters);
+    q.reason = "a last wave of " + std::to_string(last) + " of " + std::to_string(slots) +
+               " 256x256 tiles is cut off: " + q.reason + " over the first " + std::to_string(cut) +
+               (axis == 1 ? " columns" : " rows") + ", then the rest: " + rest.reason;
+    q.rest.push_back(std::move(rest));
+    p = std::move(q);
+}
+
 Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast_ok, int force,
                bool glu) {
     Plan p;
@@ -242,6 +296,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool fast
     const bool skinny = units_fit && ((force == 1) || (force == 0 && M <= 64));
     Plan q = skinny ? plan_skinny(M, W, K, dev, glu) : plan_tile(M, W, K, dev);
     q.glu = glu;
+    if (!skinny) cut_sparse_last_wave(q, M, W, K, dev, glu);
     return q;
 }
 
@@ -316,7 +371,7 @@ static const char* kernel_name(int k) {
 }
 
 std::string plan_json(const Plan& p, int64_t M, int64_t N, int64_t K) {
-    char buf[1024];
+    char buf[4096];
     snprintf(buf, sizeof buf,
              "{\"M\": %lld, \"N\": %lld, \"K\": %lld, \"kernel\": \"%s\", \"bm\": %d, \"bn\": %d, "
              "\"bk\": %d, \"threads\": %d, \"tiles_m\": %lld, \"tiles_n\": %lld, \"tiles\": %lld, "
@@ -335,7 +390,16 @@ std::string plan_json(const Plan& p, int64_t M, int64_t N, int64_t K) {
              (long long)p.ws_floats,
              p.kernel == kKernMx ? "mx" : (p.kernel == kKernPacked ? "packed" : (p.glu ? "swiglu" : "gemm")),
              p.reason.c_str());
-    return std::string(buf);
+    std::string s(buf);
+    if (p.cut_axis != 0 && !p.rest.empty()) {
+        // the strip left over: its own plan, over its own sizes
+        const int64_t Mr = p.cut_axis == 2 ? M - p.cut_at : M;
+        const int64_t Nr = p.cut_axis == 1 ? N - p.cut_at : N;
+        s.pop_back();
+        s += ", \"cut\": {\"axis\": \"" + std::string(p.cut_axis == 1 ? "n" : "m") +
+             "\", \"at\": " + std::to_string(p.cut_at) + ", \"rest\": " + plan_json(p.rest[0], Mr, Nr, K) + "}}";
+    }
+    return s;
 }
 
 }  // namespace glk

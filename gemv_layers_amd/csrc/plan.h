@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <string>
+#include <vector>
 
 namespace glk {
 
@@ -38,6 +39,13 @@ struct Plan {
     double wave_eff = 0.0;   // (grid / slots) / waves
     int64_t ws_floats = 0;   // workspace floats the launch uses
     int64_t counters = 0;    // workspace counters the launch uses
+    // A product whose last wave of 256 x 256 tiles would be at most half full is cut in two: this
+    // plan then covers the first `cut_at` output columns (cut_axis 1) or rows (cut_axis 2), and
+    // rest[0] the remaining strip, launched after it on the same stream (ws_floats and counters
+    // are then the larger of the two parts' needs).
+    int cut_axis = 0;
+    int64_t cut_at = 0;
+    std::vector<Plan> rest;
     std::string reason;
 };
 

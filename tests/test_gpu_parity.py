@@ -255,6 +255,37 @@ def test_epilogue_rounds_to_nearest_even(entry, M):
     assert np.all(C == want[None, :])
 
 
+# ---- a sparse last wave of 256 x 256 tiles cut off as a strip -----------------------------
+# (the planner keeps the whole waves' rectangle and plans the strip left over on its own; both
+# launches write C, so every row sampled crosses the column cut, and rows on both sides of a row
+# cut are sampled)
+CUT_SHAPES = [(4096, 4352, 1024, "n", 4096),   # 272 tiles: 16 in the last wave
+              (4000, 4400, 1000, "n", 4096),   # ragged M, N, K: 288 tiles
+              (4352, 4096, 1024, "m", 4096),   # a row cut keeps 256 tiles, a column cut 255
+              (8192, 8448, 512, "n", 8192)]    # after four full waves
+
+
+@pytest.mark.parametrize("M,N,K,axis,at", CUT_SHAPES)
+def test_sparse_last_wave_cut(M, N, K, axis, at):
+    A = matrix("normal", M, K, seed=7000 + M)
+    B = matrix("normal", K, N, seed=8000 + N, sigma=0.5)
+    C = run("auto", A, B, M, N, K)
+    plan = g.gemm_last_plan()
+    assert plan["bm"] == 256 and plan["cut"]["axis"] == axis and plan["cut"]["at"] == at, plan
+    assert plan["cut"]["rest"]["bm"] == 128
+    rows = np.unique(np.concatenate([_sample_rows(M, 24), [at - 1, at, min(at + 1, M - 1)]]))
+    rows = rows[rows < M]
+    ref, sabs = oracle.gemm(np.ascontiguousarray(A[rows]), B, M=len(rows), N=N, K=K)
+    res = oracle.check(np.ascontiguousarray(C[rows]), ref, sabs)
+    assert res.ok, f"cut {M}x{N}x{K} {res.summary()}"
+    Ai = matrix("int", M, K, seed=7100 + M)
+    Bi = matrix("int", K, N, seed=8100 + N)
+    Ci = run("auto", Ai, Bi, M, N, K)
+    ref, _ = oracle.gemm(np.ascontiguousarray(Ai[rows]), Bi, M=len(rows), N=N, K=K, with_abs=False)
+    bad = np.argwhere(Ci[rows] != oracle.bf16_rne(ref))
+    assert bad.size == 0, f"cut int {M}x{N}x{K}: {len(bad)} mismatches, first {bad[0].tolist()}"
+
+
 # ---- full-size workloads, in the benchmark's launch configuration -------------------------
 
 FULL = ["sq512", "sq4096", "sq8192", "sq16384", "mlp_up", "mlp_down"] + \

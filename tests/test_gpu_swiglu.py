@@ -165,6 +165,22 @@ def test_llama7b_gate_up_prefill_sampled_rows():
         assert res.ok, f"row {r}: {res.summary()}"
 
 
+def test_sparse_last_wave_cut_across_rows():
+    """4608 tokens against a 4096 x (2 x 2304) weight: 324 tiles of 256 x 256 leave a last wave of
+    68, which is cut off as a row strip (the SwiGLU form cannot take a column cut) planned on its
+    own; rows on both sides of the cut and at both ends are checked."""
+    M, N, K = 4608, 2304, 1024
+    A = matrix("normal", M, K, seed=7600)
+    B = matrix("normal", K, 2 * N, seed=7601, sigma=0.05)
+    C, plan = run(A, B, M, N, K)
+    assert plan["op"] == "swiglu" and plan["cut"]["axis"] == "m" and plan["cut"]["at"] == 3584, plan
+    assert plan["cut"]["rest"]["bm"] == 128
+    for r in (0, 1000, 3583, 3584, 3585, 4000, 4607):
+        h, slack = osw.swiglu_rows(A, B, r, 1, N, K)
+        res = osw.check(C[r: r + 1], h, slack)
+        assert res.ok, f"row {r}: {res.summary()}"
+
+
 # ---- seeded random shapes across every dispatch regime ---------------------------------------
 
 def _random_glu_cases(n, seed=20251203):

@@ -160,10 +160,17 @@ def test_swiglu_tile_plan_covers_both_halves(M, N, K):
     p = g.gemm_plan_describe(M, N, K, swiglu=True)
     q = g.gemm_plan_describe(M, 2 * N, K)
     assert p["kernel"] == "tile" and p["op"] == "swiglu" and p["N"] == N
-    for key in ("bm", "bn", "tiles_m", "tiles_n", "grid", "splits", "schedule"):
-        assert p[key] == q[key], key
+    if "cut" in q and q["cut"]["axis"] == "n":
+        # the plain product may cut a sparse last wave off as a column strip; the SwiGLU form
+        # cannot (its up half sits N weight columns after the gate half), so it keeps the tiles
+        assert "cut" not in p or p["cut"]["axis"] == "m"
+        assert p["bm"] == q["bm"] and p["tiles_m"] == q["tiles_m"]
+    else:
+        for key in ("bm", "bn", "tiles_m", "tiles_n", "grid", "splits", "schedule"):
+            assert p[key] == q[key], key
     # a BN-wide tile makes BN / 2 outputs
-    assert p["tiles_n"] == _cdiv(N, p["bn"] // 2)
+    if "cut" not in p:
+        assert p["tiles_n"] == _cdiv(N, p["bn"] // 2)
 
 
 @pytest.mark.parametrize("M", [1, 2, 16, 17, 64])
@@ -246,3 +253,63 @@ def test_tile_rules_follow_the_cu_count(cus, M, N, K):
         assert p["grid"] <= 2 * cus
         if cus // p["tiles"] >= 2:
             assert p["grid"] <= cus
+
+
+# ---- a sparse last wave of 256 x 256 tiles cut off as a strip ------------------------------
+
+@pytest.mark.parametrize("M,N,K,glu,want", [
+    (4096, 4352, 4096, False, ("n", 4096)), (4352, 4352, 4096, False, ("n", 3840)),
+    (4352, 4096, 1024, False, ("m", 4096)), (8192, 8448, 4096, False, ("n", 8192)),
+    (4608, 4608, 4608, False, ("n", 3584)), (4096, 11008, 4096, False, None),
+    (5120, 5120, 5120, False, None), (4096, 4096, 4096, False, None), (8192, 8192, 8192, False, None),
+    (4608, 2304, 4096, True, ("m", 3584)), (4096, 11008, 4096, True, None)])
+def test_sparse_last_wave_cut_at_256_cus(M, N, K, glu, want):
+    p = g.gemm_plan_describe(M, N, K, 256, swiglu=glu)
+    if want is None:
+        assert "cut" not in p, p
+    else:
+        assert (p["cut"]["axis"], p["cut"]["at"]) == want, p
+
+
+@pytest.mark.parametrize("cus", [80, 228, 256, 304])
+@pytest.mark.parametrize("M,N,K,glu", [
+    (4096, 4352, 4096, False), (4352, 4352, 4096, False), (4352, 4096, 1024, False),
+    (4000, 4400, 1000, False), (8192, 8448, 4096, False), (4608, 4608, 4608, False),
+    (6144, 6144, 6144, False), (4096, 11008, 4096, False), (2560, 3072, 2048, False),
+    (3000, 9000, 512, False), (4608, 2304, 4096, True), (4096, 11008, 4096, True),
+    (3000, 2000, 1000, True)])
+def test_sparse_last_wave_cut_rule(cus, M, N, K, glu):
+    # with the 256 x 256 tiles of a data-parallel plan leaving a last wave at most half full, the
+    # largest rectangle of whole tile rows or columns that fits in the full waves is kept (a
+    # column cut only outside the SwiGLU form) and the strip left over is planned on its own; the
+    # cut is taken only when that strip comes out as 128 x 128 tiles
+    W = 2 * N if glu else N
+    bm_, bn_ = -(-M // 256), -(-W // 256)
+    full, last = divmod(bm_ * bn_, cus)
+    tn = (full * cus) // bm_ if not glu else 0
+    tm = (full * cus) // bn_
+    cands = []
+    if not glu and 1 <= tn < bn_:
+        cands.append((tn * bm_, "n", tn * 256))
+    if 1 <= tm < bm_ and (not cands or tm * bn_ > cands[0][0]):
+        cands = [(tm * bn_, "m", tm * 256)]
+    p = g.gemm_plan_describe(M, N, K, cus, swiglu=glu)
+    uncut = p.get("cut") is None
+    sparse = p["bm"] == 256 and full >= 1 and 0 < last and 2 * last <= cus and cands
+    if not uncut:
+        kept, axis, at = cands[-1]
+        c = p["cut"]
+        assert sparse and (c["axis"], c["at"]) == (axis, at), p
+        assert p["bm"] == 256 and p["tiles"] == kept <= full * cus
+        assert c["rest"]["bm"] == 128 and c["rest"]["kernel"] == "tile"
+        if axis == "n":
+            assert c["rest"]["M"] == M and c["rest"]["N"] == N - at
+        else:
+            assert c["rest"]["M"] == M - at and c["rest"]["N"] == N
+        assert p["ws_floats"] >= c["rest"]["ws_floats"]
+    elif sparse:
+        # the strip would not have come out as small tiles
+        kept, axis, at = cands[-1]
+        rest = (g.gemm_plan_describe(M, N - at, K, cus, swiglu=glu) if axis == "n"
+                else g.gemm_plan_describe(M - at, N, K, cus, swiglu=glu))
+        assert rest["bm"] != 128 or rest["kernel"] != "tile", (p, rest)
