@@ -58,18 +58,21 @@ int gemm_init(int device);
  * and schedule chosen per call from the shape and the device's compute-unit count ("1024 cubed
  * and the decode shapes": the launch picks the tile per call). Operands whose pointers are not
  * 16-byte aligned, or whose N, K, lda, ldb, ldc are not multiples of 8, take a general kernel
- * with the same result contract.
+ * with the same result contract. When the large tiles would leave a last wave at most half full,
+ * the product is cut into a rectangle of whole waves and the strip left over, each planned on its
+ * own and launched in turn on `stream` (two kernels, no host work between them): "Kernel
+ * development on sm_120", section 4, wave quantization of the last wave.
  * M == 0 or N == 0: nothing is launched. K == 0: C is set to zero (the empty sum).
  * Errors: GEMM_ERR_INVALID_ARG for negative sizes, lda < K, ldb < N, ldc < N, or a null
  * pointer with a non-empty extent; GEMM_ERR_NOT_INITIALIZED before gemm_init; GEMM_ERR_HIP if a
  * launch fails. The call is deterministic: the same inputs give the same bits on every run.
  * Workspace: split layouts sum float32 partials in K order through slots and arrival counters
- * that the kernel itself returns to zero, so a call is one launch with no memset (spark-kernels
- * post, "stream-k proper": nothing cleared between launches; "the decode kernel": the last slice
- * resets the workspace so a call stays one launch). The slots and counters live in a region per
- * (device, stream), made on the stream's first call that needs one (hipMalloc, plus a clear on a
- * library-private stream that is waited for, so that even a first call inside a graph capture
- * records only the product's kernel). Calls on different streams therefore never share partials
+ * that the kernel itself returns to zero, so a call needs no memset (spark-kernels post,
+ * "stream-k proper": nothing cleared between launches; "the decode kernel": the last slice
+ * resets the workspace, so no clearing launch is needed). The slots and counters live in a
+ * region per (device, stream), made on the stream's first call that needs one (hipMalloc, plus a
+ * clear on a library-private stream that is waited for, so that even a first call inside a graph
+ * capture records only the product's kernels). Calls on different streams therefore never share partials
  * and may run concurrently; calls on one stream run in order. A captured graph keeps using the
  * region of the stream it was captured on, so it must not be replayed concurrently with calls on
  * that stream. At most 64 streams per device get a region; a call on a further stream that needs
