@@ -72,11 +72,11 @@ int gemm_init(int device);
  * resets the workspace, so no clearing launch is needed). The slots and counters live in a
  * region per (device, stream), made on the stream's first call that needs one (hipMalloc, plus a
  * clear on a library-private stream that is waited for, so that even a first call inside a graph
- * capture records only the product's kernels). Calls on different streams therefore never share partials
- * and may run concurrently; calls on one stream run in order. A captured graph keeps using the
- * region of the stream it was captured on, so it must not be replayed concurrently with calls on
- * that stream. At most 64 streams per device get a region; a call on a further stream that needs
- * one returns GEMM_ERR_UNSUPPORTED.
+ * capture records only the product's kernels). Calls on different streams therefore never share
+ * partials and may run concurrently; calls on one stream run in order. A captured graph keeps
+ * using the region of the stream it was captured on, so it must not be replayed concurrently
+ * with calls on that stream. At most 64 streams per device get a region; a call on a further
+ * stream that needs one returns GEMM_ERR_UNSUPPORTED.
  */
 int gemm_bf16(int64_t M, int64_t N, int64_t K,
               const void *A, int64_t lda,
