@@ -286,6 +286,29 @@ def test_sparse_last_wave_cut(M, N, K, axis, at):
     assert bad.size == 0, f"cut int {M}x{N}x{K}: {len(bad)} mismatches, first {bad[0].tolist()}"
 
 
+# Ragged products whose plan cuts a sparse last wave off, three per direction, drawn once from
+# a seeded generator (M and N uniform in 2000-9000, multiples of 8; K a multiple of 8 up to 1024,
+# so sampled rows stay cheap for the oracle) and kept as data so that collecting the tests needs
+# no library: (M, N, K, direction, position of the cut). One leaves a strip of 8 rows.
+RANDOM_CUT_CASES = [(5376, 3312, 400, "n", 3072), (4792, 3800, 992, "m", 4352),
+                    (6408, 4936, 584, "m", 6400), (4152, 8616, 320, "n", 7680),
+                    (2792, 7592, 416, "n", 5888), (5088, 4120, 304, "m", 3840)]
+
+
+@pytest.mark.parametrize("M,N,K,axis,at", RANDOM_CUT_CASES)
+def test_random_cut_shapes_integer_exact(M, N, K, axis, at):
+    Ai = matrix("int", M, K, seed=7200 + M)
+    Bi = matrix("int", K, N, seed=8200 + N)
+    C = run("auto", Ai, Bi, M, N, K)
+    plan = g.gemm_last_plan()
+    assert (plan["cut"]["axis"], plan["cut"]["at"]) == (axis, at), plan
+    rows = np.unique(np.concatenate([_sample_rows(M, 12), [at - 1, at, min(at + 1, M - 1)] if axis == "m" else []]))
+    rows = rows[(rows >= 0) & (rows < M)].astype(np.int64)
+    ref, _ = oracle.gemm(np.ascontiguousarray(Ai[rows]), Bi, M=len(rows), N=N, K=K, with_abs=False)
+    bad = np.argwhere(C[rows] != oracle.bf16_rne(ref))
+    assert bad.size == 0, f"cut int {M}x{N}x{K} {axis}@{at}: {len(bad)} mismatches, first {bad[0].tolist()}"
+
+
 # ---- full-size workloads, in the benchmark's launch configuration -------------------------
 
 FULL = ["sq512", "sq4096", "sq8192", "sq16384", "mlp_up", "mlp_down"] + \

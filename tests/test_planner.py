@@ -262,7 +262,11 @@ def test_tile_rules_follow_the_cu_count(cus, M, N, K):
     (4352, 4096, 1024, False, ("m", 4096)), (8192, 8448, 4096, False, ("n", 8192)),
     (4608, 4608, 4608, False, ("n", 3584)), (4096, 11008, 4096, False, None),
     (5120, 5120, 5120, False, None), (4096, 4096, 4096, False, None), (8192, 8192, 8192, False, None),
-    (4608, 2304, 4096, True, ("m", 3584)), (4096, 11008, 4096, True, None)])
+    (4608, 2304, 4096, True, ("m", 3584)), (4096, 11008, 4096, True, None),
+    # the seeded ragged cases of the GPU parity tests
+    (5376, 3312, 400, False, ("n", 3072)), (4792, 3800, 992, False, ("m", 4352)),
+    (6408, 4936, 584, False, ("m", 6400)), (4152, 8616, 320, False, ("n", 7680)),
+    (2792, 7592, 416, False, ("n", 5888)), (5088, 4120, 304, False, ("m", 3840))])
 def test_sparse_last_wave_cut_at_256_cus(M, N, K, glu, want):
     p = g.gemm_plan_describe(M, N, K, 256, swiglu=glu)
     if want is None:
