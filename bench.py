@@ -18,6 +18,9 @@ Alongside (reported, not part of `value`):
   the median and the minimum over rounds ("Benchmarks" page of gemm3, "Measurement conditions";
   "Kernel development on sm_120", section 6), the time with the Infinity Cache flushed before
   each launch, and its own roofline object;
+* three shapes outside those configurations, one for each planner rule that none of them
+  exercises (a sparse last wave cut off, one 128 x 128 tile per CU with K split, between one and
+  two tiles per CU), against hipBLASLt in the same rounds (planner_cases);
 * the shader clock and board power sampled every 250 ms over a sustained run of the 8192^3
   product ("the roof is the power limit");
 * every decode workload (M = 1, 2, 16, 64 against the 7B MLP weights), over 12 rotating copies of
@@ -140,6 +143,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-torch", action="store_true", help="skip the torch.matmul comparison")
     ap.add_argument("--no-power", action="store_true", help="skip the sustained power/clock sample")
+    ap.add_argument("--no-planner-cases", action="store_true",
+                    help="skip the shapes outside the configurations that show the planner's rules")
     ap.add_argument("--no-swiglu", action="store_true",
                     help="skip the fused gate/up SwiGLU workloads")
     ap.add_argument("--no-mx", action="store_true",
@@ -454,6 +459,44 @@ def main():
         if "hipblaslt_tflops_median" in hc:
             headline["torch_matmul_tflops"] = hc["hipblaslt_tflops_median"]
     out["headline"] = headline
+
+    # ---------------- shapes outside the configurations, one per planner rule ----------------
+    # (timing only, N(0,1) inputs drawn on the device; ours against hipBLASLt in the same rounds)
+    PLANNER_CASES = [("last_wave_cut", 4096, 4352, 4096),     # 272 big tiles: the last 16 cut off
+                     ("one_small_tile_per_cu", 1024, 4096, 11008),  # 256 tiles of 128 x 128, K split
+                     ("small_tiles_1_to_2_per_cu", 512, 11008, 4096)]  # 344 tiles of 128 x 128
+    if not args.no_compute and not args.no_planner_cases:
+        cases = {}
+        torch.manual_seed(0)
+        for name, M, N, K in PLANNER_CASES:
+            log(f"planner case {name} {M}x{N}x{K}")
+            At = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+            Bt = torch.randn(K, N, device="cuda").to(torch.bfloat16)
+            Ct = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            Ht = torch.empty_like(Ct)
+            arms = {"ours": lambda: g.gemm_bf16(M, N, K, P(At), K, P(Bt), N, P(Ct), N, sh)}
+            if not args.no_torch:
+                arms["hipblaslt"] = lambda: torch.matmul(At, Bt, out=Ht)
+            for f in arms.values():
+                warm(lambda i, f=f: f(), ms=RAMP_MS / 2)
+            arms["ours"]()
+            torch.cuda.synchronize()
+            pl = g.gemm_last_plan()
+            t = timed_rounds(arms, 50, args.rounds)
+            med = float(np.median(t["ours"]))
+            flops = 2.0 * M * N * K
+            rec = {"M": M, "N": N, "K": K, "us_median": round(med, 2),
+                   "tflops_median": round(flops / (med * 1e-6) / 1e12, 1),
+                   "plan": {k: pl.get(k) for k in ("bm", "bn", "grid", "schedule", "splits")},
+                   "cut": ({"axis": pl["cut"]["axis"], "at": pl["cut"]["at"],
+                            "rest": {k: pl["cut"]["rest"].get(k) for k in ("bm", "grid", "schedule", "splits")}}
+                           if "cut" in pl else None)}
+            if "hipblaslt" in t:
+                hm = float(np.median(t["hipblaslt"]))
+                rec.update({"hipblaslt_us_median": round(hm, 2), "speedup_vs_hipblaslt": round(hm / med, 3)})
+            cases[name] = rec
+            del At, Bt, Ct, Ht
+        out["planner_cases"] = cases
 
     # ---------------- clock and power over a sustained product ----------------
     if not args.no_power:
