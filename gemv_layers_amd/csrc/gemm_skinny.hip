@@ -334,7 +334,9 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(SkinnyArgs p) {
     // leaves its partial stored but unannounced: waiting for the store at once would also wait
     // for every load of the ring behind it. Vector-memory operations complete in issue order, so
     // by the time the loads of unit i + STAGES (issued after the store) have landed, the store has
-    // too, and the arrival is counted then, at no cost. Reductions wait for the range's end.
+    // too, and the arrival is counted then. (Reading the arrival's result then waits for the loads
+    // wave 0 has in flight; reading it only after the range measured slower.) Reductions wait
+    // for the range's end.
     int pend = -1, pend_at = 0;  // stored, not yet counted
     int fin = -1;                // stored at the range's last unit
     int red0 = -1, red1 = -1;    // strips this workgroup completes
