@@ -3,8 +3,9 @@
 The allocation-free entry point runs gemm_bf16's own plan and kernels with the library's fixed
 scratch array as workspace, so its output must equal gemm_bf16's bit for bit. Two calls in a row,
 the second on a smaller input, for each layout that uses the workspace (skinny K split, skinny
-Stream-K ranges, large-tile K split, one and two pieces per CU) and one that does not; every
-output is also checked against the float64 oracle. The 1664 x 1664 x 4096 split plan (169 tiles
+Stream-K ranges, large-tile K split, one and two pieces per CU, a product cut into a rectangle
+of whole waves and a K-split strip) and one that does not; every output is also checked against
+the float64 oracle. The 1664 x 1664 x 4096 split plan (169 tiles
 of 128 x 128 in 3 pieces, two per CU on most CUs) takes 8 306 688 of the array's 8 Mi floats
 (the most a plan on 256 CUs can need is 8 Mi, 512 pieces); the skinny 17 x 264 x 11008 plan
 takes 4 Mi.
@@ -52,7 +53,9 @@ PAIRS = [((17, 264, 11008), (16, 4096, 11008)),                        # every s
          ((16, 4096, 11008), (3, 4096, 4096)),                          # skinny, K split
          ((1000, 1000, 1000), (512, 512, 512)),                        # 128 x 128 tiles, K split
          ((1664, 1664, 4096), (1536, 1536, 1024)),                      # K split, two pieces per CU
-         ((4096, 4096, 4096), (300, 520, 328))]                        # 256 x 256 tiles, no split
+         ((4096, 4096, 4096), (300, 520, 328)),                        # 256 x 256 tiles, no split
+         ((4096, 4352, 1024), (4352, 4096, 512))]                       # a sparse last wave cut off
+                                                                        # (two launches, the strip K split)
 
 
 @pytest.mark.parametrize("first,second", PAIRS)
@@ -66,6 +69,8 @@ def test_noalloc_matches_gemm_bf16_twice(first, second):
             assert plan["ws_floats"] == 4 << 20
         if n == 0 and (M, N, K) == (1664, 1664, 4096):
             assert plan["splits"] == 3 and plan["ws_floats"] == 169 * 3 * 128 * 128 > 4 << 20
+        if (M, N, K) in ((4096, 4352, 1024), (4352, 4096, 512)):
+            assert "cut" in plan and plan["cut"]["rest"]["schedule"] == "split-k", plan
         got = _call(g.gemm_bf16_noalloc, A, B, M, N, K)
         assert g.gemm_last_plan() == plan
         bad = np.argwhere(got != want)
