@@ -917,7 +917,8 @@ def main():
                    "algorithmic_bytes": nbytes, "gbps": round(gbps, 1),
                    "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": MI355X_PEAK_HBM_GBPS,
                                 "unit": "GB/s", "frac": round(gbps / MI355X_PEAK_HBM_GBPS, 4)},
-                   "splits": plan.get("splits"), "grid": plan.get("grid")}
+                   "tiles_per_group": plan.get("strip", 0) // 16, "splits": plan.get("splits"),
+                   "grid": plan.get("grid")}
             if "hbm_copy_gbps" in peaks:
                 rec["frac_of_measured_copy"] = round(gbps / peaks["hbm_copy_gbps"], 4)
             bf = out.get("decode", {}).get(name, {}).get("us_graph_replay")

@@ -362,11 +362,11 @@ int mx_decode(int64_t M, int64_t N, int64_t K, const void* Aq, int64_t ldaq, con
         a.red_off = 0;
         if (fused) {
             const int piece_ks = (a.ks + p.splits - 1) / p.splits;
-            const int lds = glk::mx_fused_layout(piece_ks, a);
+            const int lds = glk::mx_fused_layout(piece_ks, p.strip / 16, a);
             if (lds < 0) return GEMM_ERR_UNSUPPORTED;
-            e = glk::launch_mx_decode_fused(a, (int)p.grid, lds, stream);
+            e = glk::launch_mx_decode_fused(p.strip / 16, a, (int)p.grid, lds, stream);
         } else {
-            e = glk::launch_mx_decode(p.mtiles, a, (int)p.grid, stream);
+            e = glk::launch_mx_decode(p.mtiles, p.strip / 16, a, (int)p.grid, stream);
         }
     }
     if (e != hipSuccess) return GEMM_ERR_HIP;
@@ -635,7 +635,7 @@ int gemm_mx_decode_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
         const glk::Plan p = glk::make_mx_plan(M, N, K, info);
         glk::MxArgs probe;
         const int ks = (int)(K / 128);
-        if (p.kernel == glk::kKernMx && glk::mx_fused_layout((ks + p.splits - 1) / p.splits, probe) >= 0) {
+        if (p.kernel == glk::kKernMx && glk::mx_fused_layout((ks + p.splits - 1) / p.splits, p.strip / 16, probe) >= 0) {
             return mx_decode(M, N, K, nullptr, K, nullptr, K / 32, Wp, Sp, C, ldc, hs, A, lda);
         }
     }

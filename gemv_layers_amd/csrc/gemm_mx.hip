@@ -152,14 +152,15 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(const uint16_t* __restric
 
 // ---- the product ---------------------------------------------------------------------------------
 
-constexpr int kMxTN = 4;  // column tiles (16 columns each) per workgroup
+// k-steps in flight per wave (measured: 2 beat 3, 4 and 6 on every decode shape)
 constexpr int kMxD = 2;
-constexpr int kMxFusedLdsMax = 160 * 1024;  // the fused form's activation rows + reduction   // k-steps in flight per wave (measured: 2 beat 3, 4 and 6 on every decode shape)
+constexpr int kMxFusedLdsMax = 160 * 1024;  // the fused form's activation rows + reduction
 
-template <int MT>
+// TN column tiles (16 columns each) per workgroup: 3 or 4, chosen by the planner
+template <int MT, int TN>
 struct MxStage {
-    u32x4 w[kMxTN];       // weight codes, lane's 16 bytes of each tile's block
-    uint32_t ws[kMxTN];   // weight scale byte
+    u32x4 w[TN];          // weight codes, lane's 16 bytes of each tile's block
+    uint32_t ws[TN];      // weight scale byte
     u32x4 a[MT][2];       // activation codes of each 16-row tile: k 16 g .. +15 and 64 + 16 g .. +15
     uint32_t as[MT];      // activation scale byte
 };
@@ -167,9 +168,9 @@ struct MxStage {
 // FUSED (M <= 2, MT = 1): the workgroup converts the bf16 activations of its K piece to MXFP8 in
 // LDS itself (while its first weight loads are in flight) and reads the activation operands from
 // there: the product from bf16 activations in one launch, with the same bits as the two-launch path.
-template <int MT, bool FUSED>
+template <int MT, bool FUSED, int TN>
 __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
-    constexpr int TN = kMxTN, D = kMxD;
+    constexpr int D = kMxD;
     static_assert(!FUSED || MT == 1, "the fused conversion serves one 16-row tile");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -204,7 +205,7 @@ __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
     }
     // every call issues the same loads, out-of-range ones at an invalid offset (they read zeros:
     // code 0 with scale byte 0 adds nothing)
-    auto load = [&](MxStage<MT>& st, int s) {
+    auto load = [&](MxStage<MT, TN>& st, int s) {
         const bool sok = s < we;
         if constexpr (FUSED) {  // activations come from LDS at compute time
 #pragma unroll
@@ -242,7 +243,7 @@ __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
     // fused: activation codes [row][k - 128 pb] at lds, scales [row][block - 4 pb] at lds + 2 kpb
     const uint8_t* aq_lds = reinterpret_cast<const uint8_t*>(lds);
     const uint8_t* as_lds = aq_lds + 2 * p.kpb;
-    auto compute = [&](MxStage<MT>& st, int s) {
+    auto compute = [&](MxStage<MT, TN>& st, int s) {
         if constexpr (FUSED) {
             const int m = i16, ls = s - pb;
             u32x4 x0 = u32x4{0u, 0u, 0u, 0u}, x1 = x0;
@@ -270,7 +271,7 @@ __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
         }
     };
 
-    MxStage<MT> st[D];
+    MxStage<MT, TN> st[D];
 #pragma unroll
     for (int j = 0; j < D; ++j) load(st[j], wb + j);
     if constexpr (FUSED) {
@@ -376,50 +377,68 @@ __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
     }
 }
 
-template <int MT, bool FUSED>
+template <int MT, bool FUSED, int TN>
 static hipError_t mx_configure_one() {
-    return hipFuncSetAttribute((const void*)mx_decode_kernel<MT, FUSED>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               FUSED ? kMxFusedLdsMax : mx_decode_lds_bytes(MT));
+    return hipFuncSetAttribute((const void*)mx_decode_kernel<MT, FUSED, TN>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               FUSED ? kMxFusedLdsMax : mx_decode_lds_bytes(MT, TN));
 }
 
-int mx_decode_lds_bytes(int mtiles) { return 4 * kMxTN * mtiles * 1024; }
-int mx_decode_tiles_per_group() { return kMxTN; }
+int mx_decode_lds_bytes(int mtiles, int tn) { return 4 * tn * mtiles * 1024; }
 
-hipError_t configure_mx_kernels() {
-    hipError_t e = mx_configure_one<1, false>();
-    if (e == hipSuccess) e = mx_configure_one<2, false>();
-    if (e == hipSuccess) e = mx_configure_one<3, false>();
-    if (e == hipSuccess) e = mx_configure_one<4, false>();
-    if (e == hipSuccess) e = mx_configure_one<1, true>();
+template <int TN>
+static hipError_t mx_configure_tn() {
+    hipError_t e = mx_configure_one<1, false, TN>();
+    if (e == hipSuccess) e = mx_configure_one<2, false, TN>();
+    if (e == hipSuccess) e = mx_configure_one<3, false, TN>();
+    if (e == hipSuccess) e = mx_configure_one<4, false, TN>();
+    if (e == hipSuccess) e = mx_configure_one<1, true, TN>();
     return e;
 }
 
-hipError_t launch_mx_decode(int mtiles, const MxArgs& a, int grid, hipStream_t s) {
-    const size_t lds = (size_t)mx_decode_lds_bytes(mtiles);
+hipError_t configure_mx_kernels() {
+    hipError_t e = mx_configure_tn<3>();
+    if (e == hipSuccess) e = mx_configure_tn<4>();
+    return e;
+}
+
+template <int TN>
+static hipError_t launch_mx_tn(int mtiles, const MxArgs& a, int grid, hipStream_t s) {
+    const size_t lds = (size_t)mx_decode_lds_bytes(mtiles, TN);
     switch (mtiles) {
-        case 1: mx_decode_kernel<1, false><<<grid, 256, lds, s>>>(a); break;
-        case 2: mx_decode_kernel<2, false><<<grid, 256, lds, s>>>(a); break;
-        case 3: mx_decode_kernel<3, false><<<grid, 256, lds, s>>>(a); break;
-        case 4: mx_decode_kernel<4, false><<<grid, 256, lds, s>>>(a); break;
+        case 1: mx_decode_kernel<1, false, TN><<<grid, 256, lds, s>>>(a); break;
+        case 2: mx_decode_kernel<2, false, TN><<<grid, 256, lds, s>>>(a); break;
+        case 3: mx_decode_kernel<3, false, TN><<<grid, 256, lds, s>>>(a); break;
+        case 4: mx_decode_kernel<4, false, TN><<<grid, 256, lds, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+hipError_t launch_mx_decode(int mtiles, int tn, const MxArgs& a, int grid, hipStream_t s) {
+    if (tn == 3) return launch_mx_tn<3>(mtiles, a, grid, s);
+    if (tn == 4) return launch_mx_tn<4>(mtiles, a, grid, s);
+    return hipErrorInvalidValue;
+}
+
 // LDS of the fused form for pieces of at most `piece_ks` k-steps, or -1 if it does not fit; sets
 // the args' activation row stride and reduction offset
-int mx_fused_layout(int piece_ks, MxArgs& a) {
+int mx_fused_layout(int piece_ks, int tn, MxArgs& a) {
     const int kpb = piece_ks * 128;
     const int red_off = (2 * kpb + 2 * (kpb / 32) + 15) / 16 * 16;
-    const int bytes = red_off + mx_decode_lds_bytes(1);
+    const int bytes = red_off + mx_decode_lds_bytes(1, tn);
     if (bytes > kMxFusedLdsMax) return -1;
     a.kpb = kpb;
     a.red_off = red_off;
     return bytes;
 }
 
-hipError_t launch_mx_decode_fused(const MxArgs& a, int grid, int lds_bytes, hipStream_t s) {
-    mx_decode_kernel<1, true><<<grid, 256, (size_t)lds_bytes, s>>>(a);
+hipError_t launch_mx_decode_fused(int tn, const MxArgs& a, int grid, int lds_bytes, hipStream_t s) {
+    if (tn == 3)
+        mx_decode_kernel<1, true, 3><<<grid, 256, (size_t)lds_bytes, s>>>(a);
+    else if (tn == 4)
+        mx_decode_kernel<1, true, 4><<<grid, 256, (size_t)lds_bytes, s>>>(a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

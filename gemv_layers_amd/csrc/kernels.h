@@ -91,7 +91,7 @@ struct MxArgs {
     int ldaq, ldas, ldc;
     int tiles;           // N / 16 column tiles
     int ks, kq;          // K / 128 k-steps; ceil(ks / 4) scale groups
-    int pieces;          // K pieces per group of mx_decode_tiles_per_group() tiles (one workgroup each)
+    int pieces;          // K pieces per group of TN column tiles (one workgroup each)
     int nxcd;            // XCDs the hardware deals workgroups over (1 = no remap)
     float* ws;           // pieces > 1: groups * pieces * 4 * mtiles * 256 floats
     uint32_t* counters;  // one per group, zero between launches
@@ -101,12 +101,12 @@ struct MxArgs {
     int lda16;
     int kpb, red_off;
 };
-int mx_decode_tiles_per_group();
-int mx_fused_layout(int piece_ks, MxArgs& a);  // LDS bytes of the fused form, or -1
-hipError_t launch_mx_decode_fused(const MxArgs& a, int grid, int lds_bytes, hipStream_t s);
-int mx_decode_lds_bytes(int mtiles);
+// tn: column tiles per workgroup, 3 or 4 (the plan's strip / 16)
+int mx_fused_layout(int piece_ks, int tn, MxArgs& a);  // LDS bytes of the fused form, or -1
+hipError_t launch_mx_decode_fused(int tn, const MxArgs& a, int grid, int lds_bytes, hipStream_t s);
+int mx_decode_lds_bytes(int mtiles, int tn);
 hipError_t configure_mx_kernels();
-hipError_t launch_mx_decode(int mtiles, const MxArgs& a, int grid, hipStream_t s);
+hipError_t launch_mx_decode(int mtiles, int tn, const MxArgs& a, int grid, hipStream_t s);
 // bf16 rows -> MX codes and scales: fp4 = false, E4M3 row-major (Q: ldq bytes per row, S: lds);
 // fp4 = true, E2M1 in the packed weight layout (rows % 16 == 0, cols % 128 == 0; ldq, lds unused)
 hipError_t launch_mx_quant(bool fp4, const uint16_t* X, int rows, int cols, int ldx, uint8_t* Q, int ldq,

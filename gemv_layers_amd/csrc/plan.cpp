@@ -348,8 +348,25 @@ static Plan decode_groups_plan(int kind, int64_t M, int64_t N, int64_t K, int64_
     return p;
 }
 
+// Workgroups of four column tiles, or of three where that spreads the weight over more CUs: the
+// product streams the weight, and a CU left without a workgroup adds nothing to the read rate
+// (11008 columns: 172 groups of four against 230 of three, 6% faster at 16 and 64 rows; 4096
+// columns: 64 groups of four in 4 K pieces fill 256 CUs exactly and stay).
 Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
-    return decode_groups_plan(kKernMx, M, N, K, K / 128, mx_decode_tiles_per_group(), dev);
+    Plan best;
+    double best_fill = -1.0;
+    for (int tn : {4, 3}) {
+        Plan q = decode_groups_plan(kKernMx, M, N, K, K / 128, tn, dev);
+        if (q.kernel != kKernMx) return q;
+        // the share of the busiest round of CUs that holds a workgroup
+        const int64_t rounds = cdiv(q.grid, (int64_t)dev.cus);
+        const double fill = (double)q.grid / (double)(rounds * dev.cus);
+        if (fill > best_fill + 1e-9) {
+            best = q;
+            best_fill = fill;
+        }
+    }
+    return best;
 }
 
 // The packed bf16 decode reads the same kind of 1 KB operand blocks over 32-k steps.

@@ -158,7 +158,7 @@ def run_decode(aq, as_, wp, sp, M, N, K, ldc=None):
 
 
 DECODE = [(1, 16, 128), (1, 64, 640), (3, 80, 512), (2, 256, 11008), (16, 4096, 4096),
-          (17, 1024, 2048), (33, 2048, 1024), (48, 512, 4096), (64, 1040, 1152)]
+          (17, 1024, 2048), (33, 2048, 1024), (48, 512, 4096), (64, 1040, 1152), (2, 2000, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE)
@@ -189,6 +189,13 @@ def test_split_and_unsplit_plans_are_both_covered():
     assert g.gemm_plan_describe(64, 11008, 4096, mx=True)["splits"] == 1
     assert g.gemm_plan_describe(2, 256, 11008, mx=True)["splits"] > 1
     assert g.gemm_plan_describe(16, 4096, 4096, mx=True)["splits"] > 1
+    # both group widths, each with a last group short of tiles, K whole and K in pieces
+    seen = set()
+    for M, N, K in DECODE:
+        p = g.gemm_plan_describe(M, N, K, mx=True)
+        tn = p["strip"] // 16
+        seen.add((tn, (N // 16) % tn != 0, p["splits"] > 1))
+    assert {(3, True, True), (3, True, False), (4, True, True), (4, True, False), (4, False, True)} <= seen
 
 
 def test_decode_bf16_pipeline_and_ldc():

@@ -191,23 +191,38 @@ def test_swiglu_skinny_plan_covers_both_halves(M):
 
 # ---- the block-scaled decode product --------------------------------------------------------
 
+def _mx_groups(tiles, K, tn):
+    """Groups of tn column tiles and K pieces as the decode plans them: K whole when the groups
+    cover 60% of the CUs, else just enough pieces to cover them all (at least 4 k-steps a piece)."""
+    strips = _cdiv(tiles, tn)
+    want = 1 if 5 * strips >= 3 * 256 else _cdiv(256, strips)
+    return strips, min(want, max(1, (K // 128) // 4))
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 11008, 4096), (16, 11008, 4096), (64, 11008, 4096),
-                                   (1, 4096, 11008), (64, 4096, 11008), (3, 80, 640)])
+                                   (1, 4096, 11008), (64, 4096, 11008), (3, 80, 640), (2, 128, 128),
+                                   (1, 12288, 4096), (1, 4096, 4096)])
 def test_mx_plan(M, N, K):
     p = g.gemm_plan_describe(M, N, K, mx=True)
     assert p["kernel"] == "mx" and p["op"] == "mx"
     tiles = N // 16
-    assert p["tiles_n"] == tiles and p["strips"] == _cdiv(tiles, 4) and p["ks"] == K // 128
-    s = p["splits"]
-    assert 1 <= s <= max(1, (K // 128) // 4)
-    assert p["grid"] == p["strips"] * s
-    # K whole when the groups cover 60% of the CUs, else just enough pieces to cover them all
-    want = 1 if 5 * p["strips"] >= 3 * 256 else _cdiv(256, p["strips"])
-    assert s == min(want, max(1, (K // 128) // 4))
+    tn = p["strip"] // 16
+    assert tn in (3, 4)
+    assert p["tiles_n"] == tiles and p["ks"] == K // 128
+    assert (p["strips"], p["splits"]) == _mx_groups(tiles, K, tn)
+    assert p["grid"] == p["strips"] * p["splits"]
+
+    # the group width whose grid leaves the fewest CUs idle in its last round; four on a tie
+    def fill(t):
+        strips, s = _mx_groups(tiles, K, t)
+        grid = strips * s
+        return grid / (_cdiv(grid, 256) * 256)
+
+    assert tn == (3 if fill(3) > fill(4) else 4)
     if (N, K) == (11008, 4096):
-        assert s == 1
+        assert (tn, p["grid"]) == (3, 230)  # 172 groups of four would leave 84 CUs idle
     if (N, K) == (4096, 11008):
-        assert s == 4
+        assert (tn, p["splits"], p["grid"]) == (4, 4, 256)
 
 
 def test_mx_plan_rejects_other_shapes():
