@@ -34,7 +34,7 @@
 //   last arriver adds them in K order and writes bf16, returning its counter to zero.
 
 #include "common.h"
-#include "kernels.h"
+#include "mx.h"
 
 namespace glk {
 

@@ -21,7 +21,7 @@
 //   order and returns its counter to zero (as the skinny kernel does).
 
 #include "common.h"
-#include "kernels.h"
+#include "packed.h"
 
 namespace glk {
 

@@ -40,7 +40,7 @@
 //   reduction are unchanged; the activation is applied where bf16 is written.
 
 #include "common.h"
-#include "kernels.h"
+#include "skinny.h"
 
 namespace glk {
 

@@ -43,7 +43,7 @@
 #include <type_traits>
 
 #include "common.h"
-#include "kernels.h"
+#include "tile.h"
 
 namespace glk {
 

@@ -106,6 +106,16 @@ static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, 
     p.ws_floats = 2 * p.grid * slot_floats;
     p.counters = p.strips;
     p.splits = (int)cdiv(p.grid, p.strips);  // pieces per strip, about
+    // With 2, 4 or 8 pieces per strip (a divisor of the XCD count) the hardware's round-robin
+    // dealing alone gives each XCD the same pieces of many strips: whole rows of one K slice of
+    // the weight, where the remap gives it all of K for a few strips, one narrow column block of
+    // each row. Measured with one or two 16-row tiles, µs: 4096 x 11008 weight 20.8 -> 20.4,
+    // 4096 x 4096 12.5 -> 11.0, 8192 x 4096 18.2 -> 16.2, 14336 x 4096 25.4 -> 24.7. Not taken at
+    // four tiles (neutral to 2% slower), for the SwiGLU form (1% slower), nor with 16 or 32
+    // pieces (1-4% slower).
+    if (!glu && p.mtiles <= 2 && p.grid == (int64_t)p.strips * p.splits && p.splits >= 2 &&
+        dev.nxcd % p.splits == 0)
+        p.nxcd = 1;
     finish_waves(p);
     p.reason = "M <= 64: weights streamed once, " + std::to_string(p.grid) +
                ((p.grid % p.strips == 0) ? " workgroups, each one piece of one strip, over "
@@ -323,7 +333,11 @@ static Plan decode_groups_plan(int kind, int64_t M, int64_t N, int64_t K, int64_
         p.reason = "K == 0: C is the empty sum";
         return p;
     }
-    p.nxcd = dev.nxcd;
+    // the block-scaled decode's groups go to the XCDs in the hardware's round-robin order: measured
+    // against keeping a group's pieces (and neighbouring groups) on one XCD, µs, same bits:
+    // 4096-wide weight at M = 1, 16, 64 9.75 -> 9.50, 10.27 -> 10.13, 19.21 -> 19.04; 11008-wide
+    // at M = 1 7.92 -> 7.62
+    p.nxcd = kind == kKernMx ? 1 : dev.nxcd;
     p.threads = 256;
     p.mtiles = (int)cdiv(M, 16);
     p.tiles_n = N / 16;

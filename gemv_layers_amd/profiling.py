@@ -43,13 +43,13 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 TILE_SOURCES = ("gemv_layers_amd/csrc/gemm_tile.hip", "gemv_layers_amd/csrc/common.h",
-                "gemv_layers_amd/csrc/kernels.h", "gemv_layers_amd/csrc/stream_k.h")
+                "gemv_layers_amd/csrc/tile.h")
 SKINNY_SOURCES = ("gemv_layers_amd/csrc/gemm_skinny.hip", "gemv_layers_amd/csrc/common.h",
-                  "gemv_layers_amd/csrc/kernels.h", "gemv_layers_amd/csrc/stream_k.h")
+                  "gemv_layers_amd/csrc/skinny.h", "gemv_layers_amd/csrc/stream_k.h")
 MX_SOURCES = ("gemv_layers_amd/csrc/gemm_mx.hip", "gemv_layers_amd/csrc/common.h",
-              "gemv_layers_amd/csrc/kernels.h")
+              "gemv_layers_amd/csrc/mx.h")
 PACKED_SOURCES = ("gemv_layers_amd/csrc/gemm_packed.hip", "gemv_layers_amd/csrc/common.h",
-                  "gemv_layers_amd/csrc/kernels.h")
+                  "gemv_layers_amd/csrc/packed.h")
 _SOURCES = {"tile": TILE_SOURCES, "skinny": SKINNY_SOURCES, "mx": MX_SOURCES, "packed": PACKED_SOURCES}
 COPY_KERNEL = r"peak_copy_kernel"
 

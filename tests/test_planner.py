@@ -138,6 +138,23 @@ def test_skinny_layout_choice(shape, want):
     assert (p["strip"], p["grid"]) == want
 
 
+@pytest.mark.parametrize("M,N,K,glu,nxcd", [
+    (1, 4096, 11008, False, 1), (16, 4096, 11008, False, 1), (32, 4096, 11008, False, 1),  # 8 pieces
+    (1, 8192, 4096, False, 1), (1, 14336, 4096, False, 1),  # 4 and 2 pieces
+    (64, 4096, 11008, False, 8),  # four 16-row tiles
+    (1, 11008, 4096, False, 8),  # 5 pieces
+    (1, 2048, 8192, False, 8), (1, 1024, 4096, False, 8),  # 16 and 32 pieces
+    (64, 11008, 4096, False, 8),  # unit ranges across strips
+    (1, 11008, 4096, True, 8), (16, 11008, 4096, True, 8)])  # SwiGLU
+def test_skinny_xcd_order(M, N, K, glu, nxcd):
+    # aligned grids whose pieces per strip divide the XCD count keep the hardware's dealing
+    # (nxcd 1: no remap) at one or two 16-row tiles of the plain product
+    p = g.gemm_plan_describe(M, N, K, 256, swiglu=glu)
+    assert p["kernel"] == "skinny" and p["nxcd"] == nxcd, p
+    if nxcd == 1:
+        assert p["grid"] == p["strips"] * p["splits"] and 8 % p["splits"] == 0 and p["splits"] >= 2
+
+
 def test_skinny_small_problem_has_one_unit_per_workgroup():
     p = g.gemm_plan_describe(3, 256, 128, 256)
     assert p["kernel"] == "skinny" and p["grid"] == 2 * 2
@@ -219,6 +236,7 @@ def test_mx_plan(M, N, K):
         return grid / (_cdiv(grid, 256) * 256)
 
     assert tn == (3 if fill(3) > fill(4) else 4)
+    assert p["nxcd"] == 1  # groups dealt to the XCDs in the hardware's order
     if (N, K) == (11008, 4096):
         assert (tn, p["grid"]) == (3, 230)  # 172 groups of four would leave 84 CUs idle
     if (N, K) == (4096, 11008):
