@@ -162,6 +162,26 @@ def test_skinny_aligned_layouts(M, N, K):
     check_exact(run("skinny", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"skinny int {M}x{N}x{K}")
 
 
+# Aligned layouts with 2, 4 or 8 pieces per strip at one or two 16-row tiles keep the hardware's
+# round-robin dealing of workgroups to XCDs (no remap): grids that are and are not multiples of 8,
+# ragged N and K.
+HW_ORDER_SHAPES = [(1, 128 * 112 + 8, 1000), (3, 128 * 64 - 8, 64 * 50 + 8), (2, 128 * 32, 64 * 100 + 24),
+                   (32, 128 * 31 + 40, 64 * 90 + 8), (9, 128 * 120, 520)]
+
+
+@pytest.mark.parametrize("M,N,K", HW_ORDER_SHAPES)
+def test_skinny_hardware_xcd_order(M, N, K):
+    plan = g.gemm_plan_describe(M, N, K, 256, 1)
+    assert plan["kernel"] == "skinny" and plan["nxcd"] == 1 and plan["grid"] == plan["strips"] * plan["splits"]
+    A = matrix("normal", M, K, seed=5300 + M)
+    B = matrix("normal", K, N, seed=6300 + N, sigma=0.02)
+    check_float(run("skinny", A, B, M, N, K), A, B, M, N, K, f"skinny {M}x{N}x{K}")
+    Ai = matrix("int", M, K, seed=7300 + M)
+    Bi = matrix("int", K, N, seed=8300 + N)
+    check_exact(run("skinny", Ai, Bi, M, N, K), Ai, Bi, M, N, K, f"skinny int {M}x{N}x{K}")
+    assert g.gemm_last_plan()["nxcd"] == 1
+
+
 GENERIC_SHAPES = [(17, 15, 63), (5, 33, 1), (70, 9, 100), (1, 1, 1), (130, 67, 255)]
 
 
