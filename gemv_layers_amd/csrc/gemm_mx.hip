@@ -18,7 +18,7 @@
 //   16 t + l % 16, k = 128 s + 32 (l / 16) + j, two per byte, even j low: exactly the operand a
 //   lane hands to v_mfma_scale_f32_16x16x128_f8f6f4, so one 1 KB load per wave needs no shuffle.
 //   The scales of four k-steps of a tile share 256 bytes, lane l owning byte 4 l + s % 4.
-// * mx_decode_kernel: a workgroup takes TN = 4 column tiles and one of S pieces of their k-steps;
+// * mx_decode_kernel: a workgroup takes TN = 3 or 4 column tiles and one of S pieces of their k-steps;
 //   its 4 waves take contiguous quarters of the piece and run independently: no LDS and no
 //   barrier in the loop. Each wave keeps D = 2 k-steps of weights, activations and scales in flight
 //   in registers (the loads of step s + D go out as step s is consumed), and issues one scaled
@@ -175,7 +175,9 @@ __global__ void __launch_bounds__(256) mx_decode_kernel(MxArgs p) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wg = xcd_remap((int)blockIdx.x, (int)gridDim.x, p.nxcd);  // pieces of a group: one XCD
+    // logical workgroup: nxcd > 1 keeps a group's pieces on one XCD; the planner passes 1 (the
+    // hardware's round-robin order, measured faster)
+    const int wg = xcd_remap((int)blockIdx.x, (int)gridDim.x, p.nxcd);
     const int group = wg / p.pieces, piece = wg - group * p.pieces;
     // k-steps of the piece, then of this wave (contiguous quarters)
     const int pb = (int)(((int64_t)p.ks * piece) / p.pieces);
