@@ -155,6 +155,17 @@ def test_skinny_xcd_order(M, N, K, glu, nxcd):
         assert p["grid"] == p["strips"] * p["splits"] and 8 % p["splits"] == 0 and p["splits"] >= 2
 
 
+@pytest.mark.parametrize("cus", [80, 228, 256, 304])
+@pytest.mark.parametrize("M,N,K,glu", [(1, 4096, 11008, False), (16, 8192, 4096, False), (32, 14336, 4096, False),
+                                       (64, 4096, 11008, False), (1, 11008, 4096, True), (2, 2048, 8192, False)])
+def test_skinny_xcd_order_follows_the_cu_count(cus, M, N, K, glu):
+    p = g.gemm_plan_describe(M, N, K, cus, swiglu=glu)
+    dev_nxcd = 8 if cus % 8 == 0 else 1  # the XCD count the library assumes without a device
+    hw_order = (not glu and p["mtiles"] <= 2 and p["grid"] == p["strips"] * p["splits"]
+                and p["splits"] >= 2 and dev_nxcd % p["splits"] == 0)
+    assert p["nxcd"] == (1 if hw_order else dev_nxcd), p
+
+
 def test_skinny_small_problem_has_one_unit_per_workgroup():
     p = g.gemm_plan_describe(3, 256, 128, 256)
     assert p["kernel"] == "skinny" and p["grid"] == 2 * 2
@@ -208,12 +219,30 @@ def test_swiglu_skinny_plan_covers_both_halves(M):
 
 # ---- the block-scaled decode product --------------------------------------------------------
 
-def _mx_groups(tiles, K, tn):
+def _mx_groups(tiles, K, tn, cus=256):
     """Groups of tn column tiles and K pieces as the decode plans them: K whole when the groups
     cover 60% of the CUs, else just enough pieces to cover them all (at least 4 k-steps a piece)."""
     strips = _cdiv(tiles, tn)
-    want = 1 if 5 * strips >= 3 * 256 else _cdiv(256, strips)
+    want = 1 if 5 * strips >= 3 * cus else _cdiv(cus, strips)
     return strips, min(want, max(1, (K // 128) // 4))
+
+
+@pytest.mark.parametrize("cus", [80, 228, 256, 304])
+@pytest.mark.parametrize("M,N,K", [(1, 11008, 4096), (64, 4096, 11008), (1, 12288, 4096), (16, 1040, 1152),
+                                   (1, 65520, 65536)])
+def test_mx_group_width_follows_the_cu_count(cus, M, N, K):
+    # the width whose grid leaves the fewest CUs idle in its last round of CUs, four on a tie
+    p = g.gemm_plan_describe(M, N, K, cus, mx=True)
+    tiles = N // 16
+
+    def fill(t):
+        strips, s = _mx_groups(tiles, K, t, cus)
+        grid = strips * s
+        return grid / (_cdiv(grid, cus) * cus)
+
+    tn = 3 if fill(3) > fill(4) + 1e-9 else 4
+    assert p["strip"] == 16 * tn, p
+    assert (p["strips"], p["splits"]) == _mx_groups(tiles, K, tn, cus)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 11008, 4096), (16, 11008, 4096), (64, 11008, 4096),
