@@ -781,3 +781,82 @@ def test_random_shapes_integer_exact(case):
     C = run(entry, A, B, M, N, K, ldc=ldc)
     kernel = g.gemm_last_plan()["kernel"]
     check_exact(C, A, B, M, N, K, f"{entry} {M}x{N}x{K} ld {lda},{ldb},{ldc} ({kernel})")
+
+
+def _large_random_cases(n, seed=0x50A4):
+    """Seeded shapes at prefill and decode scale through gemm_bf16: decode (M <= 64, N up to
+    16000, K up to 12000), mid-size grids of small tiles with or without a K split, large grids,
+    and products with a sparse last wave of 256 x 256 tiles (a whole number of waves plus up to
+    half of one, so the planner cuts the product in two); 85% on the fast kernels (multiples of
+    8, padded leading dimensions), the rest on the general kernel."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        kind = str(rng.choice(["decode", "mid", "big", "cut"], p=[0.3, 0.25, 0.2, 0.25]))
+        if kind == "decode":
+            M, N, K = int(rng.integers(1, 65)), int(rng.integers(8, 16000)), int(rng.integers(8, 12000))
+        elif kind == "mid":
+            M, N, K = int(rng.integers(65, 2200)), int(rng.integers(64, 6000)), int(rng.integers(64, 6000))
+        elif kind == "big":
+            M, N, K = int(rng.integers(2000, 7000)), int(rng.integers(2000, 9000)), int(rng.integers(64, 3000))
+        else:
+            w, tm = int(rng.integers(1, 4)), int(rng.integers(8, 33))
+            tn = -(-256 * w // tm) + int(rng.integers(1, max(2, 128 // tm + 1)))
+            M, N = 256 * tm - int(rng.integers(0, 200)), 256 * tn - int(rng.integers(0, 200))
+            K = int(rng.integers(64, 2500))
+        if rng.random() < 0.85:
+            N, K = max(8, N - N % 8), max(8, K - K % 8)
+            pads = [0, 0, 8, 64]
+        else:
+            pads = [0, 1, 3, 13]
+        lda, ldb, ldc = (d + int(rng.choice(pads)) for d in (K, N, N))
+        cases.append((kind, M, N, K, lda, ldb, ldc))
+    return cases
+
+
+LARGE_RANDOM_CASES = _large_random_cases(64)
+
+
+def test_large_random_cases_reach_every_regime():
+    """The drawn cases include products the planner cuts in two, split-K and unsplit tiles,
+    skinny layouts in both XCD orders and the general kernel (checked on the host)."""
+    seen = set()
+    for kind, M, N, K, lda, ldb, ldc in LARGE_RANDOM_CASES:
+        if not all(x % 8 == 0 for x in (N, K, lda, ldb, ldc)):
+            seen.add("generic")
+            continue
+        p = g.gemm_plan_describe(M, N, K)
+        if "cut" in p:
+            seen.add("cut " + p["cut"]["axis"])
+        if p["kernel"] == "tile":
+            seen.add("split-k" if p["schedule"] == "split-k" else "tile")
+        if p["kernel"] == "skinny":
+            seen.add("skinny hardware order" if p["nxcd"] == 1 else "skinny remapped")
+    assert seen >= {"generic", "cut n", "cut m", "split-k", "tile", "skinny hardware order", "skinny remapped"}, seen
+
+
+@pytest.mark.parametrize("case", range(len(LARGE_RANDOM_CASES)))
+def test_large_random_shapes_integer_exact(case):
+    """Integer operands in {-4 .. 4} with NaN padding: on sampled rows (both sides of a row cut
+    among them) every column equals the oracle's exact sum rounded to bf16, and C's padding
+    columns keep their poison."""
+    kind, M, N, K, lda, ldb, ldc = LARGE_RANDOM_CASES[case]
+    A = matrix("int", M, K, seed=30000 + case, ld=lda)
+    B = matrix("int", K, N, seed=40000 + case, ld=ldb)
+    Cd = torch.empty(-(-max(M * ldc, 8) // 8) * 8, dtype=torch.bfloat16, device="cuda")
+    g.gemm_fill_launch(ctypes.c_void_p(Cd.data_ptr()), Cd.numel() * 2, POISON)
+    C = run("auto", A, B, M, N, K, ldc=ldc, C=Cd)
+    plan = g.gemm_last_plan()
+    rows = set(_sample_rows(M, 12).tolist())
+    if "cut" in plan and plan["cut"]["axis"] == "m":
+        at = plan["cut"]["at"]
+        rows |= {at - 1, at, min(M - 1, at + 1)}
+    rows = np.array(sorted(rows))
+    ref, _ = oracle.gemm(np.ascontiguousarray(A[rows, :K]), np.ascontiguousarray(B[:, :N]), M=len(rows), N=N, K=K,
+                         with_abs=False)
+    bad = np.argwhere(C[rows] != oracle.bf16_rne(ref))
+    what = f"{kind} {M}x{N}x{K} ld {lda},{ldb},{ldc} {plan['kernel']} cut={plan.get('cut', {}).get('at')}"
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[0].tolist()}"
+    if ldc > N:
+        full = host(Cd)[: M * ldc].reshape(M, ldc)
+        assert np.all(full[rows, N:] == 0x7FC0), f"{what}: padding written"
