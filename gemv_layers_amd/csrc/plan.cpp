@@ -109,7 +109,7 @@ static Plan plan_skinny(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, 
     // With 2, 4 or 8 pieces per strip (a divisor of the XCD count) the hardware's round-robin
     // dealing alone gives each XCD the same pieces of many strips: whole rows of one K slice of
     // the weight, where the remap gives it all of K for a few strips, one narrow column block of
-    // each row. Measured with one or two 16-row tiles, µs: 4096 x 11008 weight 20.8 -> 20.4,
+    // each row. Measured with one or two 16-row tiles, us: 4096 x 11008 weight 20.8 -> 20.4,
     // 4096 x 4096 12.5 -> 11.0, 8192 x 4096 18.2 -> 16.2, 14336 x 4096 25.4 -> 24.7. Not taken at
     // four tiles (neutral to 2% slower), for the SwiGLU form (1% slower), nor with 16 or 32
     // pieces (1-4% slower).
@@ -334,7 +334,7 @@ static Plan decode_groups_plan(int kind, int64_t M, int64_t N, int64_t K, int64_
         return p;
     }
     // the block-scaled decode's groups go to the XCDs in the hardware's round-robin order: measured
-    // against keeping a group's pieces (and neighbouring groups) on one XCD, µs, same bits:
+    // against keeping a group's pieces (and neighbouring groups) on one XCD, us, same bits:
     // 4096-wide weight at M = 1, 16, 64 9.75 -> 9.50, 10.27 -> 10.13, 19.21 -> 19.04; 11008-wide
     // at M = 1 7.92 -> 7.62
     p.nxcd = kind == kKernMx ? 1 : dev.nxcd;
@@ -372,7 +372,7 @@ Plan make_mx_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     for (int tn : {4, 3}) {
         Plan q = decode_groups_plan(kKernMx, M, N, K, K / 128, tn, dev);
         if (q.kernel != kKernMx) return q;
-        // the share of the busiest round of CUs that holds a workgroup
+        // how full the rounds of CUs are: the grid over rounds x CUs
         const int64_t rounds = cdiv(q.grid, (int64_t)dev.cus);
         const double fill = (double)q.grid / (double)(rounds * dev.cus);
         if (fill > best_fill + 1e-9) {
