@@ -256,7 +256,9 @@ int gemm_bf16_packed(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
  * gemm_plan_describe: host-only. Writes, as a JSON object, the plan the library would use for an
  * M x N x K product on a device with `cus` compute units (tile, grid, schedule, split count,
  * wave count and wave efficiency = (tiles/slots)/ceil(tiles/slots), the quantity of "Kernel
- * development on sm_120", section 4, budget 4). `flags` is 0 for gemm_bf16, a combination of
+ * development on sm_120", section 4, budget 4; "nxcd": 1 where workgroups keep the hardware's
+ * round-robin XCD order, else the XCD count the tile order is remapped over; for a product cut
+ * in two, "cut": the axis, the offset and the rest's own plan). `flags` is 0 for gemm_bf16, a combination of
  * GEMM_PLAN_SKINNY and GEMM_PLAN_SWIGLU, or GEMM_PLAN_MX or GEMM_PLAN_PACKED alone. Touches no HIP state. Returns
  * GEMM_ERR_INVALID_ARG for bad sizes, unknown flags or a buffer too small (buf is always
  * NUL-terminated when len > 0), GEMM_ERR_UNSUPPORTED for GEMM_PLAN_SKINNY with M outside 1 .. 64
